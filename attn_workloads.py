@@ -1,0 +1,121 @@
+"""Seeded synthetic workloads for the attention forward pass.
+
+This module is shared by the tests, the benchmark and smoke check.  It draws
+inputs and sample rows and holds the table of workload shapes; it contains none
+of the attention arithmetic, so neither the CPU oracle nor the HIP library
+depends on the other through it.
+
+Recipe (identical for every consumer):
+  * numpy ``default_rng(seed)``, seed = 1000 + workload index;
+  * Q, K, V drawn in that order as iid N(0, 1) float32 of shape [B, H, N, d];
+  * outlier workloads then draw one U[0,1) mask for Q and one for K; entries with
+    U < fraction are multiplied by ``factor`` (V is left untouched);
+  * the float32 values are cast to fp16/bf16 with round-to-nearest-even by torch
+    on the CPU.  Every consumer reads these cast tensors.
+
+The shapes follow the long-sequence attention the pages motivate tiling with
+(Triton in depth, section 3.1: sequences of 32K tokens and more) and the
+causal rule of the forward kernel (section 3.3).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str                     # "fp16" | "bf16"
+    causal_modes: tuple            # causal flags to run (1 = causal)
+    scale: float
+    seed: int
+    outlier_fraction: float = 0.0  # fraction of Q and K entries scaled up
+    outlier_factor: float = 1.0
+    sample_rows: int | None = None  # rows per head the oracle checks (None = all)
+    note: str = field(default="", compare=False)
+
+    @property
+    def shape(self):
+        return (self.B, self.H, self.N, self.d)
+
+    def flops(self, causal: int) -> float:
+        """4*B*H*N^2*d, halved when causal (the accounting used for TFLOP/s)."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2.0 if causal else f
+
+    def algorithmic_bytes(self) -> int:
+        """Q, K, V read once, O written once (2-byte elements) and lse written as fp32."""
+        elems = self.B * self.H * self.N * self.d
+        return 4 * elems * 2 + self.B * self.H * self.N * 4
+
+
+WORKLOADS = [
+    Workload("causal_b1_h1_n128_d64_fp16", 1, 1, 128, 64, "fp16", (1,), 1.0 / math.sqrt(64), 1000,
+             note="single tile, latency-bound"),
+    Workload("causal_b4_h16_n1024_d64_fp16", 4, 16, 1024, 64, "fp16", (1,), 1.0 / 8.0, 1001),
+    Workload("causal_b2_h32_n4096_d128_bf16", 2, 32, 4096, 128, "bf16", (1,), 1.0 / math.sqrt(128), 1002,
+             note="headline workload"),
+    Workload("long_b1_h16_n32768_d128_bf16", 1, 16, 32768, 128, "bf16", (1, 0), 1.0 / math.sqrt(128), 1003,
+             sample_rows=512, note="oracle checks 512 sampled rows per head"),
+    Workload("ragged_b3_h8_n3000_d80_fp16", 3, 8, 3000, 80, "fp16", (0,), 1.0 / math.sqrt(80), 1004,
+             outlier_fraction=0.01, outlier_factor=20.0, note="N not a tile multiple; 1% x20 outliers in Q, K"),
+]
+
+HEADLINE = 2  # index of the workload the benchmark reports
+
+
+def by_name(name: str) -> Workload:
+    for w in WORKLOADS:
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
+def draw_fp32(shape, seed: int, outlier_fraction: float = 0.0, outlier_factor: float = 1.0):
+    """Q, K, V as float32 numpy arrays following the recipe above."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    if outlier_fraction > 0.0:
+        mq = rng.random(shape, dtype=np.float32) < outlier_fraction
+        mk = rng.random(shape, dtype=np.float32) < outlier_fraction
+        q[mq] *= np.float32(outlier_factor)
+        k[mk] *= np.float32(outlier_factor)
+    return q, k, v
+
+
+def make_inputs(shape, dtype: str, seed: int, outlier_fraction: float = 0.0, outlier_factor: float = 1.0):
+    """Q, K, V as contiguous CPU torch tensors of the given 16-bit dtype (RNE cast)."""
+    q, k, v = draw_fp32(shape, seed, outlier_fraction, outlier_factor)
+    tdt = DTYPES[dtype]
+    return tuple(torch.from_numpy(x).to(tdt).contiguous() for x in (q, k, v))
+
+
+def workload_inputs(w: Workload):
+    return make_inputs(w.shape, w.dtype, w.seed, w.outlier_fraction, w.outlier_factor)
+
+
+def sample_rows(B: int, H: int, N: int, count: int, seed: int) -> np.ndarray:
+    """Per-head sorted query rows [B, H, count]: rows 0 and N-1 forced in, the rest drawn
+    without replacement from a seeded generator."""
+    count = min(count, N)
+    rng = np.random.default_rng(seed)
+    out = np.empty((B, H, count), dtype=np.int64)
+    for b in range(B):
+        for h in range(H):
+            forced = np.unique(np.array([0, N - 1], dtype=np.int64))
+            rest_pool = np.setdiff1d(np.arange(N, dtype=np.int64), forced)
+            rest = rng.choice(rest_pool, size=count - forced.size, replace=False)
+            out[b, h] = np.sort(np.concatenate([forced, rest]))
+    return out
