@@ -1,0 +1,175 @@
+"""Benchmark of the fused exact-attention forward on one MI355X.
+
+One step = one attn_fwd call over the whole workload (default: causal
+B=2 H=32 N=4096 d=128 bf16), inputs resident in HBM before timing starts.
+Prints ONE JSON line: TFLOP/s (4*B*H*N^2*d, halved for causal) with the
+roofline of the kernel against the dense bf16/fp16 MFMA peak and the CPU
+oracle's throughput on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--causal 0|1]
+                    [--no-cpu-baseline] [--cpu-seconds S]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak, causal N=4096 d=128"
+MFMA_PEAK_TFLOPS = 2516.6      # dense fp16/bf16: 256 CU x 4096 FLOP/clk x 2.4 GHz (the 2.5 PFLOP/s figure)
+KERNEL_SOURCE = os.path.join(ROOT, "exact_tiled_attention_03_amd", "csrc", "attn_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str, causal: int):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or None when
+    absent or when the kernel source changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = t.get(f"{workload}-causal{causal}")
+    if not entry or entry.get("source_sha256_16") != source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def cpu_baseline(w, causal, q, k, v, out, lse, budget_s: float):
+    """Time the float64 oracle on whole heads of the same workload until ~budget_s
+    of CPU work; also re-check the GPU output of those heads against it."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
+        oc, lc = out.cpu().double().numpy(), lse.cpu().double().numpy()
+        flops_per_head = w.flops(causal) / (w.B * w.H)
+        heads, t0, max_err, lse_err = 0, time.perf_counter(), 0.0, 0.0
+        rows = None
+        if w.N > 8192:   # long sequences: the oracle's rows are sampled per head
+            rows = np.sort(np.random.default_rng(w.seed + 11).choice(w.N, 256, replace=False))
+        for idx in range(w.B * w.H):
+            b, h = divmod(idx, w.H)
+            O, L = oracle.attention(qc[b:b + 1, h:h + 1], kc[b:b + 1, h:h + 1], vc[b:b + 1, h:h + 1],
+                                    causal, w.scale, rows=rows)
+            sel = slice(None) if rows is None else rows
+            max_err = max(max_err, float(np.abs(oc[b, h][sel] - O[0, 0]).max()))
+            lse_err = max(lse_err, float(np.abs(lc[b, h][sel] - L[0, 0]).max()))
+            heads += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+    if rows is None:
+        flops = heads * flops_per_head
+        sample = f"{heads} of {w.B * w.H} heads, all {w.N} rows each"
+    else:
+        # causal rows cost in proportion to their key count
+        keys = (rows + 1).sum() if causal else len(rows) * w.N
+        flops = heads * 4.0 * keys * w.d
+        sample = f"{heads} of {w.B * w.H} heads, {len(rows)} seeded rows each"
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 3), "host_cpus": cores,
+            "parity_of_timed_output": {"max_abs": max_err, "lse_max_abs": lse_err}}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="workload name (default: the headline workload)")
+    ap.add_argument("--causal", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(heads or query tiles would shard across GPUs with no exchange); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attn_workloads as aw
+    import exact_tiled_attention_03_amd as eta
+
+    w = aw.by_name(args.workload) if args.workload else aw.WORKLOADS[aw.HEADLINE]
+    causal = w.causal_modes[0] if args.causal is None else args.causal
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in aw.workload_inputs(w))
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        eta.attn_fwd(q, k, v, out, lse, causal, w.scale, stream=stream)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        eta.attn_fwd(q, k, v, out, lse, causal, w.scale, stream=stream)
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+
+    total_ms = t_begin.elapsed_time(t_end)
+    per_launch = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_per_step = total_ms / args.steps
+    launch_ms = statistics.mean(per_launch)
+    flops = w.flops(causal)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (launch_ms * 1e-3) / 1e12
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded iid N(0,1) Q, K, V)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": causal,
+                   "scale": w.scale, "layout": "[B,H,N,d] contiguous", "pct_of_mfma_peak": round(100 * value / MFMA_PEAK_TFLOPS, 2),
+                   "launch_ms_median": round(statistics.median(per_launch), 5),
+                   "launch_ms_p95": round(sorted(per_launch)[int(0.95 * (len(per_launch) - 1))], 5),
+                   "launch_ms_min": round(min(per_launch), 5)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_PEAK_TFLOPS, 4), "traffic": measured_traffic(w.name, causal),
+                     "kernel": f"attn_fwd_kernel<{w.d},{'bf16' if w.dtype == 'bf16' else 'f16'},{'causal' if causal else 'full'}>",
+                     "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": w.algorithmic_bytes()},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, causal, q, k, v, out, lse, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,108 @@
+"""Python binding of the fused exact-attention forward library (libattn.so, gfx950).
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels behind the C ABI declared in include/attn.h.  torch is used for
+device memory and the current stream.  If the compiled library is missing the
+binding raises; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn.so")
+
+ATTN_F16 = 0
+ATTN_BF16 = 1
+ATTN_OK = 0
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"attn_fwd failed with status {status}: {msg}")
+        self.status = status
+
+
+def load_library():
+    """Load libattn.so (built by __graft_entry__.build()); raise if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.attn_fwd.restype = ctypes.c_int
+    lib.attn_fwd.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                             ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                             ctypes.c_int, ctypes.c_void_p]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_status_string.argtypes = [ctypes.c_int]
+    _lib = lib
+    return lib
+
+
+def attn_status_string(status: int) -> str:
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float16:
+        return ATTN_F16
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float16 or bfloat16")
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def attn_fwd(q, k, v, out, lse, causal: bool, scale: float, stream=None) -> None:
+    """Enqueue the forward pass on `stream` (default: torch's current stream).
+
+    q, k, v, out: contiguous [B, H, N, d] float16/bfloat16 tensors on the GPU.
+    lse: contiguous [B, H, N] float32 tensor on the GPU, or None.
+    Raises AttnError with the library's status on rejected arguments."""
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    for name, t in (("k", k), ("v", v), ("out", out)):
+        if tuple(t.shape) != (B, H, N, d):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(B, H, N, d)}")
+        if t.dtype != q.dtype:
+            raise TypeError(f"{name} dtype {t.dtype} differs from q dtype {q.dtype}")
+    tensors = [q, k, v, out] + ([lse] if lse is not None else [])
+    for t in tensors:
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if lse is not None:
+        import torch
+        if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N):
+            raise ValueError("lse must be float32 [B, H, N]")
+    st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                      lse.data_ptr() if lse is not None else None,
+                      B, H, N, d, int(bool(causal)), float(scale), _dtype_code(q), _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, attn_status_string(st))
+
+
+def attention(q, k, v, causal: bool, scale: float, stream=None):
+    """Allocate out [B,H,N,d] and lse [B,H,N] with torch, then call attn_fwd."""
+    import torch
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    attn_fwd(q, k, v, out, lse, causal, scale, stream)
+    return out, lse
+
+
+__all__ = ["attn_fwd", "attn_status_string", "attention", "load_library", "AttnError", "ATTN_F16", "ATTN_BF16"]

@@ -1,0 +1,96 @@
+/*
+ * attn.h -- C ABI of the fused exact-attention forward library (MI355X, gfx950).
+ *
+ * The operation is the exact attention forward pass
+ *
+ *     O = softmax(scale * Q K^T  [+ causal mask]) V,   lse = ln sum_j exp(scale * q_i . k_j)
+ *
+ * as defined by "Triton in depth: from matmul to Flash Attention" (ybb.press),
+ * section 3.1 (the standard attention it replaces), computed the way its
+ * section 3.2 describes (Q, K and V split into tiles, running row statistics
+ * m and l, O(N) extra memory, exact result) and its section 3.3 kernel shows
+ * (one work unit per query tile and head, a loop over key/value tiles, the
+ * causal rule "key index <= query index", rescaling of the accumulator when
+ * the running max grows, one division by l after the loop).  The logsumexp
+ * output is an addition of this library; it is what a later merge of
+ * key-sharded partial results needs.
+ *
+ * Every function is plain C: pointers, integers and a float.  No allocation,
+ * no synchronisation and no global state beyond a per-device architecture
+ * cache happen inside the library.
+ */
+#ifndef ETA_ATTN_H
+#define ETA_ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and out. */
+typedef enum {
+    ATTN_F16 = 0,  /* IEEE binary16 */
+    ATTN_BF16 = 1  /* bfloat16 */
+} attn_dtype;
+
+/* Return codes.  On any code other than ATTN_OK nothing has been written and
+ * nothing has been launched, except ATTN_ERR_LAUNCH (the launch itself failed). */
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,      /* q, k, v or out is NULL */
+    ATTN_ERR_SHAPE = 2,     /* B, H or N < 1, or the launch grid would exceed 2^31-1 work-groups */
+    ATTN_ERR_HEAD_DIM = 3,  /* d is not one of 64, 80, 128 */
+    ATTN_ERR_DTYPE = 4,     /* dtype is not an attn_dtype value */
+    ATTN_ERR_SCALE = 5,     /* scale is NaN or infinite */
+    ATTN_ERR_ALIGN = 6,     /* q, k, v or out not 16-byte aligned, or lse not 4-byte aligned */
+    ATTN_ERR_DEVICE = 7,    /* no current HIP device, or it is not a gfx950 */
+    ATTN_ERR_LAUNCH = 8,    /* the kernel launch returned an error */
+    ATTN_ERR_CAUSAL = 9,    /* causal is neither 0 nor 1 */
+    ATTN_ERR_ALIAS = 10     /* out or lse overlaps q, k, v, or each other */
+} attn_status;
+
+/*
+ * attn_fwd -- fused exact-attention forward on the current HIP device.
+ *
+ *   q, k, v : device pointers, contiguous row-major [B, H, N, d] of `dtype`
+ *             (element (b,h,i,c) at offset ((b*H + h)*N + i)*d + c).  Read only.
+ *   out     : device pointer, contiguous [B, H, N, d] of `dtype`.  Every element
+ *             is written: out[b,h,i,:] = sum_j softmax_j(scale * q_i . k_j) v_j,
+ *             rounded to nearest even from an fp32 accumulator.
+ *   lse     : device pointer to contiguous [B, H, N] float32, or NULL to skip it.
+ *             lse[b,h,i] = ln sum_{j allowed} exp(scale * q_i . k_j), natural log.
+ *   B, H, N : batch, heads, sequence length (queries = keys = N), each >= 1.
+ *   d       : head dimension, one of 64, 80, 128.
+ *   causal  : 1 keeps key j for query i iff j <= i (top-left aligned, diagonal
+ *             kept); 0 keeps every key.
+ *   scale   : score scale, any finite float (usually 1/sqrt(d)); applied in fp32
+ *             to the fp32 dot products (inputs are never pre-scaled in 16 bit).
+ *   dtype   : attn_dtype of q, k, v and out.
+ *   stream  : a hipStream_t cast to void*, or NULL for the null stream.  The call
+ *             only enqueues work on it and returns without waiting; the caller
+ *             synchronises before reading out or lse.  Faults during execution
+ *             surface at that synchronisation, not here.
+ *
+ * Ownership: the caller owns every buffer; all must live on the current device
+ * and stay valid until the work on `stream` completes.  out and lse must not
+ * overlap the inputs or each other.  The library allocates nothing and keeps
+ * no reference after the call returns.
+ *
+ * Arithmetic: fp16/bf16 products with fp32 accumulation for both Q K^T and P V;
+ * probabilities are rounded to `dtype` before P V.  Results are deterministic
+ * run to run (no atomics).
+ *
+ * Returns ATTN_OK or an attn_status error code; argument checks run on the
+ * host before any device work, so an error leaves out and lse untouched.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+             int B, int H, int N, int d, int causal, float scale, int dtype,
+             void* stream);
+
+/* Static, NUL-terminated English description of a status code (never NULL). */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ETA_ATTN_H */
