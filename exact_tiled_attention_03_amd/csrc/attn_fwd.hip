@@ -35,7 +35,9 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cfloat>
 #include <cstring>
+#include <type_traits>
 
 #include "attn.h"
 
@@ -48,6 +50,17 @@ typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+// Compile-time tuning knobs (defaults are the shipped configuration).
+#ifndef ETA_WAVES_PER_EU
+#define ETA_WAVES_PER_EU 2      // waves per SIMD the register budget is sized for
+#endif
+#ifndef ETA_RESCALE_TH
+#define ETA_RESCALE_TH 8.0f     // log2 headroom before the running max is raised
+#endif
+#ifndef ETA_LANE_SWAP
+#define ETA_LANE_SWAP 1         // 1: v_permlane32_swap for the lane-pair exchange, 0: ds_bpermute
+#endif
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -96,12 +109,36 @@ struct FwdArgs {
     unsigned qsign;    // 0x80008000 when scale < 0 (Q negated exactly), else 0
 };
 
+// Value of x in the lane 32 positions away (the other half of the same accumulator column).
+__device__ __forceinline__ float pair_max(float x) {
+#if ETA_LANE_SWAP
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+#else
+    return fmaxf(x, __shfl_xor(x, 32));
+#endif
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+#if ETA_LANE_SWAP
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+#else
+    return x + __shfl_xor(x, 32);
+#endif
+}
+
 // Row of the K tile that feeds A-operand row m of the score MFMA.  With this
 // permutation, accumulator register i of a lane in half h holds key
 // 16*(i/8) + 8*h + (i%8) of the 32-key block.
 __device__ __forceinline__ int kperm(int m) {
     return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
 }
+
+// Byte stride of a V row in LDS.  The P.V operand is read with the gfx950
+// transpose load, 4 rows x 64 bytes per 32 lanes; a stride that is 64 or 192
+// modulo 256 puts those 4 rows on disjoint bank ranges.
+constexpr int v_row_bytes(int d) { return (d * 2) % 256 == 128 || (d * 2) % 256 == 0 ? d * 2 + 64 : d * 2 + 32; }
 
 // Tile configuration shared by the kernel and the host launcher.
 template <int D> struct Cfg {
@@ -112,23 +149,34 @@ template <int D> struct Cfg {
     static constexpr int SB = BN / 32;                // 32-key score blocks per tile
     static constexpr int KSTEPS = D / 16;             // MFMA k-steps over the head dim
     static constexpr int DBLK = (D + 31) / 32;        // 32-row blocks of O^T
-    static constexpr int DPAD = DBLK * 32;
     static constexpr int CPR = D / 8;                 // 16-byte chunks per row
-    static constexpr int KSTRIDE = D * 2 + 16;        // bytes per K row in LDS (one pad chunk)
-    static constexpr int VSTRIDE = BN * 2 + 16;       // bytes per V^T row in LDS
-    static constexpr int KBUF = BN * KSTRIDE;
-    static constexpr int VBUF = DPAD * VSTRIDE;
+    static constexpr int KROW = D * 2 + 16;           // bytes per K row in LDS (one pad chunk)
+    static constexpr int VROW = v_row_bytes(D);       // bytes per V row in LDS
+    static constexpr int KBUF = BN * KROW;
+    static constexpr int VBUF = BN * VROW;
     static constexpr int STAGE = KBUF + VBUF;
     static constexpr int LDS = 2 * STAGE;
-    static constexpr int KCH = BN * CPR;              // 16-byte chunks in a K tile
-    static constexpr int KIT = (KCH + NT - 1) / NT;
-    static constexpr int VG = (BN / 4) * CPR;         // 4-key x 8-column groups in a V tile
-    static constexpr int VIT = (VG + NT - 1) / NT;
+    static constexpr int CH = BN * CPR;               // 16-byte chunks in a K (or V) tile
+    static constexpr int IT = (CH + NT - 1) / NT;     // chunks per thread per tile
     static_assert(D % 16 == 0, "head dim must be a multiple of 16");
+    static_assert(VROW >= DBLK * 64, "transpose reads of the padded head dim stay inside a row");
 };
 
+typedef __fp16 lds_v4h_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __attribute__((address_space(3))) lds_v4h_t* lds_v4h_ptr;
+
+// 8 bytes from LDS through the gfx950 transpose read: within each 16-lane
+// group, lane i receives element (i % 4) of the 8-byte rows addressed by lanes
+// i/4, i/4 + 4, i/4 + 8, i/4 + 12.
+__device__ __forceinline__ u32x2_t lds_read_tr(const unsigned char* p) {
+    const lds_v4h_t t = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+        (lds_v4h_ptr)(__attribute__((address_space(3))) unsigned char*)(p));
+    return __builtin_bit_cast(u32x2_t, t);
+}
+
 template <int D, int DT, bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ETA_WAVES_PER_EU, ETA_WAVES_PER_EU)))
+void attn_fwd_kernel(FwdArgs a) {
     using C = Cfg<D>;
     using E = Elem<DT>;
     constexpr int BN = C::BN, SB = C::SB, KSTEPS = C::KSTEPS, DBLK = C::DBLK, CPR = C::CPR;
@@ -136,7 +184,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int hf = lane >> 5;   // which half of the 64-lane wave
     const int n = lane & 31;    // accumulator column = query within the wave's 32
 
@@ -172,63 +220,32 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
     const int kend = CAUSAL ? min(N, q0 + C::BM) : N;
     const int nt = (kend + BN - 1) / BN;
 
-    // ---- global -> register staging for one K/V tile
-    u32x4_t kreg[C::KIT];
-    u32x4_t vreg[C::VIT][4];
+    // ---- K/V tiles: global -> registers -> LDS (rows padded, natural layout)
+    u32x4_t kreg[C::IT], vreg[C::IT];
     auto gload = [&](int j) {
         const int kt0 = j * BN;
 #pragma unroll
-        for (int it = 0; it < C::KIT; ++it) {
+        for (int it = 0; it < C::IT; ++it) {
             const int ch = tid + it * C::NT;
-            if (C::KCH % C::NT == 0 || ch < C::KCH) {
+            if (C::CH % C::NT == 0 || ch < C::CH) {
                 const int row = ch / CPR, col = ch - (ch / CPR) * CPR;
                 const int key = kt0 + row;
-                kreg[it] = key < N ? Kh[(size_t)key * CPR + col] : u32x4_t{0, 0, 0, 0};
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < C::VIT; ++it) {
-            const int g = tid + it * C::NT;
-            if (C::VG % C::NT == 0 || g < C::VG) {
-                const int kg = g % (BN / 4), dc = g / (BN / 4);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int key = kt0 + 4 * kg + r;
-                    vreg[it][r] = key < N ? Vh[(size_t)key * CPR + dc] : u32x4_t{0, 0, 0, 0};
-                }
+                const size_t off = (size_t)key * CPR + col;
+                kreg[it] = key < N ? Kh[off] : u32x4_t{0, 0, 0, 0};
+                vreg[it] = key < N ? Vh[off] : u32x4_t{0, 0, 0, 0};
             }
         }
     };
-    // ---- register staging -> LDS stage `buf` (K row-major, V transposed)
     auto lstore = [&](int buf) {
         unsigned char* kb = smem + buf * C::STAGE;
         unsigned char* vb = kb + C::KBUF;
 #pragma unroll
-        for (int it = 0; it < C::KIT; ++it) {
+        for (int it = 0; it < C::IT; ++it) {
             const int ch = tid + it * C::NT;
-            if (C::KCH % C::NT == 0 || ch < C::KCH) {
+            if (C::CH % C::NT == 0 || ch < C::CH) {
                 const int row = ch / CPR, col = ch - (ch / CPR) * CPR;
-                *reinterpret_cast<u32x4_t*>(kb + row * C::KSTRIDE + col * 16) = kreg[it];
-            }
-        }
-#pragma unroll
-        for (int it = 0; it < C::VIT; ++it) {
-            const int g = tid + it * C::NT;
-            if (C::VG % C::NT == 0 || g < C::VG) {
-                const int kg = g % (BN / 4), dc = g / (BN / 4);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int w = e >> 1;
-                    unsigned lo, hi;
-                    if (e & 1) {
-                        lo = (vreg[it][0][w] >> 16) | (vreg[it][1][w] & 0xffff0000u);
-                        hi = (vreg[it][2][w] >> 16) | (vreg[it][3][w] & 0xffff0000u);
-                    } else {
-                        lo = (vreg[it][0][w] & 0xffffu) | (vreg[it][1][w] << 16);
-                        hi = (vreg[it][2][w] & 0xffffu) | (vreg[it][3][w] << 16);
-                    }
-                    *reinterpret_cast<u32x2_t*>(vb + (dc * 8 + e) * C::VSTRIDE + kg * 8) = u32x2_t{lo, hi};
-                }
+                *reinterpret_cast<u32x4_t*>(kb + row * C::KROW + col * 16) = kreg[it];
+                *reinterpret_cast<u32x4_t*>(vb + row * C::VROW + col * 16) = vreg[it];
             }
         }
     };
@@ -237,10 +254,86 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
     f32x16_t o[DBLK];
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) o[db] = f32x16_t{};
-    float m = kNegInf;   // running max of scale*log2(e)*score, shared by both halves
-    float l = 0.f;       // running sum over this half's keys
+    float m = kNegInf;   // reference max of scale*log2(e)*score, shared by both halves
+    float l = 0.f;       // sum over this half's keys of exp2(t - m)
     const float c = a.c;
-    const int krow = kperm(n);
+    // LDS byte offsets of this lane's operands
+    const int koff = kperm(n) * C::KROW + hf * 16;
+    const int g16 = lane >> 4, s16 = lane & 15;
+    const int voff = (8 * (g16 >> 1) + (s16 >> 2)) * C::VROW + (16 * (g16 & 1) + 4 * (s16 & 3)) * 2;
+
+    // One K/V tile for this wave; need_mask (wave-uniform) on diagonal/ragged tiles.
+    auto tile = [&](bool need_mask, const unsigned char* kb, const unsigned char* vb, int kt0) {
+        // S^T = K Q^T: two independent 32-key accumulators, interleaved
+        f32x16_t s[SB];
+#pragma unroll
+        for (int sb = 0; sb < SB; ++sb) s[sb] = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+            for (int sb = 0; sb < SB; ++sb) {
+                const u32x4_t av = *reinterpret_cast<const u32x4_t*>(kb + koff + sb * 32 * C::KROW + ks * 32);
+                s[sb] = E::mfma(av, qf[ks], s[sb]);
+            }
+
+        if (need_mask) {
+            // key index of register i is kt0 + 8*hf + 32*sb + 16*(i/8) + i%8; it is
+            // kept iff that is <= lim (the query for causal, N-1 for the tail)
+            const int lim = (CAUSAL ? min(qi, N - 1) : N - 1) - (kt0 + 8 * hf);
+#pragma unroll
+            for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (32 * sb + 16 * (i >> 3) + (i & 7) > lim) s[sb][i] = kNegInf;
+        }
+
+        // online softmax.  m is raised only when a tile's max exceeds it by more
+        // than ETA_RESCALE_TH (log2 units), so p <= 2^TH and the O rescale is rare;
+        // m, l and O always refer to the same m, so the result is unchanged.
+        float mx = kNegInf;
+#pragma unroll
+        for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
+        const float mt = pair_max(mx) * c;           // c > 0, so -inf stays -inf
+        const bool grow = mt > m + ETA_RESCALE_TH;
+        const float mnew = grow ? mt : m;
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;   // 0 when m was -inf
+        m = mnew;
+        const float nm = m > kNegInf ? -m : 0.f;
+
+        u32x4_t pf[2 * SB];   // P^T as B operands of the P.V k-steps (16 keys each)
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sb = 0; sb < SB; ++sb) {
+            float p[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][i], c, nm));
+                part[i & 3] += p[i];
+            }
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                pf[2 * sb + hh] = u32x4_t{E::pack2(p[8 * hh + 0], p[8 * hh + 1]), E::pack2(p[8 * hh + 2], p[8 * hh + 3]),
+                                          E::pack2(p[8 * hh + 4], p[8 * hh + 5]), E::pack2(p[8 * hh + 6], p[8 * hh + 7])};
+        }
+        l = l * alpha + ((part[0] + part[1]) + (part[2] + part[3]));
+
+        if (__any(grow)) {
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) o[db] *= alpha;
+        }
+        // O^T += V^T P^T; V^T operand = two transpose reads of 4 keys each
+#pragma unroll
+        for (int kk = 0; kk < 2 * SB; ++kk)
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) {
+                const unsigned char* vp = vb + voff + 16 * kk * C::VROW + db * 64;
+                const u32x2_t lo = lds_read_tr(vp);
+                const u32x2_t hi = lds_read_tr(vp + 4 * C::VROW);
+                o[db] = E::mfma(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pf[kk], o[db]);
+            }
+    };
 
     gload(0);
     lstore(0);
@@ -251,81 +344,11 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
         if (j + 1 < nt) gload(j + 1);
 
         const int kt0 = j * BN;
-        const bool active = qw0 < N && (!CAUSAL || kt0 <= qw0 + 31);
-        if (active) {
+        // tiles wholly above this wave's diagonal, or waves past N, do no math
+        if (qw0 < N && (!CAUSAL || kt0 <= qw0 + 31)) {
             const unsigned char* kb = smem + buf * C::STAGE;
             const unsigned char* vb = kb + C::KBUF;
-
-            // S^T = K Q^T
-            f32x16_t s[SB];
-#pragma unroll
-            for (int sb = 0; sb < SB; ++sb) {
-                s[sb] = f32x16_t{};
-                const unsigned char* kr = kb + (sb * 32 + krow) * C::KSTRIDE + hf * 16;
-#pragma unroll
-                for (int ks = 0; ks < KSTEPS; ++ks) {
-                    const u32x4_t av = *reinterpret_cast<const u32x4_t*>(kr + ks * 32);
-                    s[sb] = E::mfma(av, qf[ks], s[sb]);
-                }
-            }
-
-            // masks: only diagonal tiles (causal) and the ragged last tile
-            const bool need_mask = (CAUSAL && kt0 + BN - 1 > qw0) || (kt0 + BN > N);
-            auto masked = [&](int sb, int i) {
-                const int key = kt0 + sb * 32 + 16 * (i >> 3) + 8 * hf + (i & 7);
-                return key >= N || (CAUSAL && key > qi);
-            };
-
-            // online softmax
-            float mraw = kNegInf;
-            if (need_mask) {
-#pragma unroll
-                for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, masked(sb, i) ? kNegInf : s[sb][i]);
-            } else {
-#pragma unroll
-                for (int sb = 0; sb < SB; ++sb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) mraw = fmaxf(mraw, s[sb][i]);
-            }
-            mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
-            const float mt = mraw > kNegInf ? mraw * c : kNegInf;
-            const float mnew = fmaxf(m, mt);
-            const float muse = mnew > kNegInf ? mnew : 0.f;
-            const float alpha = __builtin_amdgcn_exp2f(m - muse);
-            m = mnew;
-
-            u32x4_t pf[2 * SB];   // P^T as B operands of the P.V k-steps (16 keys each)
-            float rs = 0.f;
-#pragma unroll
-            for (int sb = 0; sb < SB; ++sb) {
-                float p[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][i], c, -muse));
-                    if (need_mask) e = masked(sb, i) ? 0.f : e;
-                    p[i] = e;
-                    rs += e;
-                }
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh)
-                    pf[2 * sb + hh] = u32x4_t{E::pack2(p[8 * hh + 0], p[8 * hh + 1]), E::pack2(p[8 * hh + 2], p[8 * hh + 3]),
-                                              E::pack2(p[8 * hh + 4], p[8 * hh + 5]), E::pack2(p[8 * hh + 6], p[8 * hh + 7])};
-            }
-            l = l * alpha + rs;
-
-            // O^T = alpha * O^T + V^T P^T
-#pragma unroll
-            for (int db = 0; db < DBLK; ++db) {
-                o[db] *= alpha;
-                const unsigned char* vr = vb + (db * 32 + n) * C::VSTRIDE + hf * 16;
-#pragma unroll
-                for (int kk = 0; kk < 2 * SB; ++kk) {
-                    const u32x4_t av = *reinterpret_cast<const u32x4_t*>(vr + kk * 32);
-                    o[db] = E::mfma(av, pf[kk], o[db]);
-                }
-            }
+            tile((CAUSAL && kt0 + BN - 1 > qw0) || kt0 + BN > N, kb, vb, kt0);
         }
 
         if (j + 1 < nt) lstore(buf ^ 1);
@@ -334,7 +357,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(FwdArgs a) {
 
     // ---- epilogue: O = acc / l, lse = ln2 * (m + log2 l)
     if (qw0 < N) {
-        const float ltot = l + __shfl_xor(l, 32);
+        const float ltot = pair_sum(l);
         if (qi < N) {
             const float inv = 1.0f / ltot;
             uint16_t* orow = a.o + ((size_t)bh * N + qi) * D;
@@ -435,7 +458,9 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
     a.N = N;
     a.BH = (int)bh;
     a.nqt = (int)nqt;
-    a.c = std::fabs(scale) * kLog2e;
+    // c must be > 0 so that masked scores (-inf) map to -inf; scale == 0 uses the
+    // smallest normal float, which makes every exponent round to exactly 0
+    a.c = scale == 0.f ? FLT_MIN : std::fabs(scale) * kLog2e;
     a.qsign = std::signbit(scale) && scale != 0.f ? 0x80008000u : 0u;
 
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -70,17 +70,20 @@ def assert_within_derived_bound(out, lse, q, k, v, causal, scale, rows=None, lab
         u * sum_j w_j |v_j|  +  u * (|O| + u * sum_j w_j |v_j|),
     which exceeds 1e-2 for bf16 when a few keys with large |v| dominate a row
     (early causal rows).  Each element must be within max(1e-2, that bound plus
-    1e-5 * (1 + sum_j w_j |v_j|) of fp32 accumulation slack); mean-abs and lse
-    keep the plain bar."""
+    1e-5 * (1 + sum_j w_j |v_j|) of fp32 accumulation slack); the mean error must
+    be within max(1e-3, the mean of the same bound), since with very few keys the
+    output rounding alone averages about 1e-3 in bf16; lse keeps the plain bar."""
     u = unit_roundoff(q.dtype)
     O, L = oracle.attention(q, k, v, causal, scale, rows=rows)
     A, _ = oracle.attention(q, k, v.abs(), causal, scale, rows=rows)
     og = gather_rows(out.double().numpy(), rows)
     e = np.abs(og - O)
-    bound = np.maximum(MAX_ABS, u * A + u * (np.abs(O) + u * A) + 1e-5 * (1.0 + A))
+    derived = u * A + u * (np.abs(O) + u * A) + 1e-5 * (1.0 + A)
+    bound = np.maximum(MAX_ABS, derived)
     worst = np.unravel_index(np.argmax(e - bound), e.shape)
     assert (e <= bound).all(), f"{label} error {e[worst]:.3e} > bound {bound[worst]:.3e} at {worst}"
-    assert e.mean() <= MEAN_ABS, f"{label} mean_abs {e.mean():.3e} > {MEAN_ABS}"
+    mean_bar = max(MEAN_ABS, float(derived.mean()))
+    assert e.mean() <= mean_bar, f"{label} mean_abs {e.mean():.3e} > {mean_bar:.3e}"
     if lse is not None:
         lerr = np.abs(gather_rows(lse.double().numpy(), rows) - L).max()
         assert lerr <= LSE_ABS, f"{label} lse error {lerr:.3e} > {LSE_ABS}"
