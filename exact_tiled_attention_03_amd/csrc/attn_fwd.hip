@@ -135,12 +135,19 @@ __device__ __forceinline__ int kperm(int m) {
     return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
 }
 
-// Byte stride of a V row in LDS.  The P.V operand is read with the gfx950
-// transpose load, 4 rows x 64 bytes per 32 lanes; a stride that is 64 or 192
-// modulo 256 puts those 4 rows on disjoint bank ranges.
-constexpr int v_row_bytes(int d) { return (d * 2) % 256 == 128 || (d * 2) % 256 == 0 ? d * 2 + 64 : d * 2 + 32; }
-
 // Tile configuration shared by the kernel and the host launcher.
+//
+// LDS holds two stages of K and V, each a BN x ROWB byte array written by
+// direct global->LDS loads: one load instruction of a wave fills 1 KB of
+// consecutive 16-byte slots, so rows are unpadded (ROWB = CPRP * 16 with CPRP
+// the chunk count rounded up to a power of two) and bank conflicts are avoided
+// by XOR-swizzling the 16-byte chunk index with a function of the row:
+//  * K is read by the score MFMA as 16-byte chunks of 16 different rows at the
+//    same logical chunk: chunk c of row r sits at c ^ kswz(r), kswz(r) =
+//    (r / RPB) % CPRP with RPB rows per 256-byte bank line.
+//  * V is read by 8-byte transpose loads, 4 consecutive rows x one 64-byte
+//    granule per 32 lanes: the granule index g of row r sits at
+//    g ^ ((r / RPB) % GPR), GPR granules per row.
 template <int D> struct Cfg {
     static constexpr int WAVES = 4;
     static constexpr int NT = 64 * WAVES;             // threads per work-group
@@ -149,38 +156,48 @@ template <int D> struct Cfg {
     static constexpr int SB = BN / 32;                // 32-key score blocks per tile
     static constexpr int KSTEPS = D / 16;             // MFMA k-steps over the head dim
     static constexpr int DBLK = (D + 31) / 32;        // 32-row blocks of O^T
-    static constexpr int CPR = D / 8;                 // 16-byte chunks per row
-    static constexpr int KROW = D * 2 + 16;           // bytes per K row in LDS (one pad chunk)
-    static constexpr int VROW = v_row_bytes(D);       // bytes per V row in LDS
-    static constexpr int KBUF = BN * KROW;
-    static constexpr int VBUF = BN * VROW;
-    static constexpr int STAGE = KBUF + VBUF;
-    static constexpr int LDS = 2 * STAGE;
-    static constexpr int CH = BN * CPR;               // 16-byte chunks in a K (or V) tile
-    static constexpr int IT = (CH + NT - 1) / NT;     // chunks per thread per tile
-    static_assert(D % 16 == 0, "head dim must be a multiple of 16");
-    static_assert(VROW >= DBLK * 64, "transpose reads of the padded head dim stay inside a row");
+    static constexpr int CPR = D / 8;                 // 16-byte chunks per row in HBM
+    static constexpr int CPRP = CPR <= 8 ? 8 : 16;    // chunks per row in LDS
+    static constexpr int ROWB = CPRP * 16;            // bytes per row in LDS
+    static constexpr int RPB = 256 / ROWB;            // rows per 256-byte bank line
+    static constexpr int GPR = CPRP / 4;              // 64-byte granules per row
+    static constexpr int TILEB = BN * ROWB;           // bytes of one K or V tile
+    static constexpr int KOFF = 0;                    // K stage s at KOFF + s * TILEB
+    static constexpr int VOFF = 2 * TILEB;            // V stage s at VOFF + s * TILEB
+    static constexpr int LDS = 4 * TILEB;
+    static constexpr int IT = TILEB / (16 * NT);      // direct-load instructions per tile and thread
+    static_assert(D % 16 == 0 && CPR <= CPRP, "head dim");
+    static_assert(TILEB % (16 * NT) == 0, "a tile is a whole number of load rounds");
+    static_assert(DBLK <= GPR, "transpose reads of the padded head dim stay inside a row");
+    static_assert(VOFF + 2 * TILEB <= 65536, "LDS offsets fit the 16-bit immediate");
 };
 
 typedef __fp16 lds_v4h_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
 typedef __attribute__((address_space(3))) lds_v4h_t* lds_v4h_ptr;
+typedef __attribute__((address_space(3))) unsigned char* lds_bytes;
 
 // 8 bytes from LDS through the gfx950 transpose read: within each 16-lane
 // group, lane i receives element (i % 4) of the 8-byte rows addressed by lanes
 // i/4, i/4 + 4, i/4 + 8, i/4 + 12.
-__device__ __forceinline__ u32x2_t lds_read_tr(const unsigned char* p) {
-    const lds_v4h_t t = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-        (lds_v4h_ptr)(__attribute__((address_space(3))) unsigned char*)(p));
+__device__ __forceinline__ u32x2_t lds_read_tr(unsigned addr) {
+    const lds_v4h_t t = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_v4h_ptr)(lds_bytes)(size_t)addr);
     return __builtin_bit_cast(u32x2_t, t);
+}
+
+__device__ __forceinline__ u32x4_t lds_read16(unsigned addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>((lds_bytes)(size_t)addr);
 }
 
 template <int D, int DT, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ETA_WAVES_PER_EU, ETA_WAVES_PER_EU)))
 void attn_fwd_kernel(FwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
     using C = Cfg<D>;
     using E = Elem<DT>;
     constexpr int BN = C::BN, SB = C::SB, KSTEPS = C::KSTEPS, DBLK = C::DBLK, CPR = C::CPR;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[C::LDS];
+    constexpr int CPRP = C::CPRP, ROWB = C::ROWB;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS];
+    const unsigned lds0 = (unsigned)(size_t)(lds_bytes)smem;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -202,14 +219,11 @@ void attn_fwd_kernel(FwdArgs a) {
     const int qw0 = q0 + wave * 32;
     const int qi = qw0 + n;
     const size_t hoff = (size_t)bh * (size_t)N * CPR;   // head offset in 16-byte chunks
-    const u32x4_t* Qh = a.q + hoff;
-    const u32x4_t* Kh = a.k + hoff;
-    const u32x4_t* Vh = a.v + hoff;
 
     // ---- Q fragments (B operand of S^T = K Q^T), loaded once
     u32x4_t qf[KSTEPS];
     if (qi < N) {
-        const u32x4_t* src = Qh + (size_t)qi * CPR + hf;
+        const u32x4_t* src = a.q + hoff + (size_t)qi * CPR + hf;
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = src[2 * ks] ^ a.qsign;
     } else {
@@ -220,35 +234,52 @@ void attn_fwd_kernel(FwdArgs a) {
     const int kend = CAUSAL ? min(N, q0 + C::BM) : N;
     const int nt = (kend + BN - 1) / BN;
 
-    // ---- K/V tiles: global -> registers -> LDS (rows padded, natural layout)
-    u32x4_t kreg[C::IT], vreg[C::IT];
-    auto gload = [&](int j) {
+    // ---- direct global -> LDS loads.  Slot (it, wave, lane) of a tile holds
+    // row r = slot / CPRP, physical chunk p = slot % CPRP, i.e. logical chunk
+    // p ^ swizzle(r); chunks past the head dim get an out-of-range offset and
+    // read as zero, as do rows past N (the buffer ends at row N).
+    unsigned kvo[C::IT], vvo[C::IT];
+#pragma unroll
+    for (int it = 0; it < C::IT; ++it) {
+        const int slot = it * C::NT + wave * 64 + lane;
+        const int r = slot / CPRP, p = slot % CPRP;
+        const int kc = p ^ ((r / C::RPB) % CPRP);
+        const int vc = p ^ (4 * ((r / C::RPB) % C::GPR));
+        kvo[it] = kc < CPR ? (unsigned)(r * D * 2 + kc * 16) : 0x80000000u;
+        vvo[it] = vc < CPR ? (unsigned)(r * D * 2 + vc * 16) : 0x80000000u;
+    }
+    const unsigned char* kbase = reinterpret_cast<const unsigned char*>(a.k + hoff);
+    const unsigned char* vbase = reinterpret_cast<const unsigned char*>(a.v + hoff);
+    auto issue_loads = [&](int j, int stage) {
         const int kt0 = j * BN;
+        const int bytes = (N - kt0) * D * 2;            // rows kt0 .. N-1 are in range
+        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (size_t)kt0 * D * 2), 0, bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (size_t)kt0 * D * 2), 0, bytes, 0x00020000);
 #pragma unroll
         for (int it = 0; it < C::IT; ++it) {
-            const int ch = tid + it * C::NT;
-            if (C::CH % C::NT == 0 || ch < C::CH) {
-                const int row = ch / CPR, col = ch - (ch / CPR) * CPR;
-                const int key = kt0 + row;
-                const size_t off = (size_t)key * CPR + col;
-                kreg[it] = key < N ? Kh[off] : u32x4_t{0, 0, 0, 0};
-                vreg[it] = key < N ? Vh[off] : u32x4_t{0, 0, 0, 0};
-            }
+            const unsigned dst = (unsigned)((it * C::NT + wave * 64) * 16);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void*)(lds_bytes)(size_t)(lds0 + C::KOFF + stage * C::TILEB + dst), 16, kvo[it], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(lds_bytes)(size_t)(lds0 + C::VOFF + stage * C::TILEB + dst), 16, vvo[it], 0, 0, 0);
         }
     };
-    auto lstore = [&](int buf) {
-        unsigned char* kb = smem + buf * C::STAGE;
-        unsigned char* vb = kb + C::KBUF;
+
+    // ---- per-lane LDS read addresses (stage 0; stage 1 adds TILEB)
+    unsigned ka[KSTEPS];   // score A operand: row kperm(n), logical chunk 2*ks + hf
+    {
+        const int r = kperm(n);
+        const int x = (r / C::RPB) % CPRP;
 #pragma unroll
-        for (int it = 0; it < C::IT; ++it) {
-            const int ch = tid + it * C::NT;
-            if (C::CH % C::NT == 0 || ch < C::CH) {
-                const int row = ch / CPR, col = ch - (ch / CPR) * CPR;
-                *reinterpret_cast<u32x4_t*>(kb + row * C::KROW + col * 16) = kreg[it];
-                *reinterpret_cast<u32x4_t*>(vb + row * C::VROW + col * 16) = vreg[it];
-            }
-        }
-    };
+        for (int ks = 0; ks < KSTEPS; ++ks) ka[ks] = lds0 + C::KOFF + r * ROWB + (((2 * ks + hf) ^ x) * 16);
+    }
+    unsigned va[DBLK];     // P.V A operand via transpose reads (see lds_read_tr)
+    {
+        const int g16 = lane >> 4, s16 = lane & 15;
+        const int r = 8 * (g16 >> 1) + (s16 >> 2);           // + 16*kk + 4*half, both multiples of 4
+        const int x = (r / C::RPB) % C::GPR;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+            va[db] = lds0 + C::VOFF + r * ROWB + (4 * (db ^ x) + 2 * (g16 & 1) + ((s16 & 3) >> 1)) * 16 + 8 * (s16 & 1);
+    }
 
     // ---- per-lane running state (one query row per lane, half the keys)
     f32x16_t o[DBLK];
@@ -257,13 +288,10 @@ void attn_fwd_kernel(FwdArgs a) {
     float m = kNegInf;   // reference max of scale*log2(e)*score, shared by both halves
     float l = 0.f;       // sum over this half's keys of exp2(t - m)
     const float c = a.c;
-    // LDS byte offsets of this lane's operands
-    const int koff = kperm(n) * C::KROW + hf * 16;
-    const int g16 = lane >> 4, s16 = lane & 15;
-    const int voff = (8 * (g16 >> 1) + (s16 >> 2)) * C::VROW + (16 * (g16 & 1) + 4 * (s16 & 3)) * 2;
 
     // One K/V tile for this wave; need_mask (wave-uniform) on diagonal/ragged tiles.
-    auto tile = [&](bool need_mask, const unsigned char* kb, const unsigned char* vb, int kt0) {
+    auto tile = [&](auto stage_tag, bool need_mask, int kt0) {
+        constexpr int ST = decltype(stage_tag)::value * C::TILEB;
         // S^T = K Q^T: two independent 32-key accumulators, interleaved
         f32x16_t s[SB];
 #pragma unroll
@@ -271,10 +299,8 @@ void attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
-            for (int sb = 0; sb < SB; ++sb) {
-                const u32x4_t av = *reinterpret_cast<const u32x4_t*>(kb + koff + sb * 32 * C::KROW + ks * 32);
-                s[sb] = E::mfma(av, qf[ks], s[sb]);
-            }
+            for (int sb = 0; sb < SB; ++sb)
+                s[sb] = E::mfma(lds_read16(ka[ks] + ST + sb * 32 * ROWB), qf[ks], s[sb]);
 
         if (need_mask) {
             // key index of register i is kt0 + 8*hf + 32*sb + 16*(i/8) + i%8; it is
@@ -328,31 +354,30 @@ void attn_fwd_kernel(FwdArgs a) {
         for (int kk = 0; kk < 2 * SB; ++kk)
 #pragma unroll
             for (int db = 0; db < DBLK; ++db) {
-                const unsigned char* vp = vb + voff + 16 * kk * C::VROW + db * 64;
-                const u32x2_t lo = lds_read_tr(vp);
-                const u32x2_t hi = lds_read_tr(vp + 4 * C::VROW);
+                const u32x2_t lo = lds_read_tr(va[db] + ST + 16 * kk * ROWB);
+                const u32x2_t hi = lds_read_tr(va[db] + ST + (16 * kk + 4) * ROWB);
                 o[db] = E::mfma(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pf[kk], o[db]);
             }
     };
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
-    for (int j = 0; j < nt; ++j) {
-        const int buf = j & 1;
-        if (j + 1 < nt) gload(j + 1);
-
+    // one loop step: prefetch tile j+1 into the other stage, compute tile j, sync
+    auto step = [&](auto stage_tag, int j) {
+        constexpr int STAGE = decltype(stage_tag)::value;
+        if (j + 1 < nt) issue_loads(j + 1, STAGE ^ 1);
         const int kt0 = j * BN;
         // tiles wholly above this wave's diagonal, or waves past N, do no math
-        if (qw0 < N && (!CAUSAL || kt0 <= qw0 + 31)) {
-            const unsigned char* kb = smem + buf * C::STAGE;
-            const unsigned char* vb = kb + C::KBUF;
-            tile((CAUSAL && kt0 + BN - 1 > qw0) || kt0 + BN > N, kb, vb, kt0);
-        }
-
-        if (j + 1 < nt) lstore(buf ^ 1);
+        if (qw0 < N && (!CAUSAL || kt0 <= qw0 + 31))
+            tile(stage_tag, (CAUSAL && kt0 + BN - 1 > qw0) || kt0 + BN > N, kt0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
+    };
+
+    issue_loads(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    for (int j = 0; j < nt; j += 2) {
+        step(std::integral_constant<int, 0>{}, j);
+        if (j + 1 < nt) step(std::integral_constant<int, 1>{}, j + 1);
     }
 
     // ---- epilogue: O = acc / l, lse = ln2 * (m + log2 l)
@@ -375,6 +400,7 @@ void attn_fwd_kernel(FwdArgs a) {
             if (a.lse != nullptr && hf == 0) a.lse[(size_t)bh * N + qi] = (m + __builtin_amdgcn_logf(ltot)) * kLn2;
         }
     }
+#endif
 }
 
 // --- host side ---------------------------------------------------------------
@@ -436,6 +462,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
     const int bm = Cfg<128>::BM;   // the same for every head dim
     const long long nqt = ((long long)N + bm - 1) / bm;
     if (bh > INT32_MAX || nqt * bh > INT32_MAX) return ATTN_ERR_SHAPE;
+    if ((long long)N * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;   // one head must fit a 32-bit buffer range
     const size_t tensor_bytes = (size_t)bh * (size_t)N * (size_t)d * 2u;
     if ((size_t)bh * (size_t)N * (size_t)d > (size_t)INT64_MAX / 4) return ATTN_ERR_SHAPE;
     const size_t lse_bytes = (size_t)bh * (size_t)N * 4u;
