@@ -8,6 +8,11 @@ oracle's throughput on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--causal 0|1]
                     [--no-cpu-baseline] [--cpu-seconds S]
+
+Traffic calibration (run each under rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE):
+    python bench.py --copy-calibration          # plain 256 MiB copy kernel, known bytes
+    python bench.py --traffic-summary ATTN_FETCH ATTN_WRITE COPY_FETCH COPY_WRITE
+        reads the four rocprofv3 output directories and writes profiles/traffic.json
 """
 from __future__ import annotations
 
@@ -45,6 +50,57 @@ def measured_traffic(workload: str, causal: int):
     if not entry or entry.get("source_sha256_16") != source_hash():
         return None
     return entry.get("bytes_per_launch")
+
+
+COPY_BYTES = 256 << 20
+
+
+def copy_calibration(steps: int):
+    """A plain device copy of COPY_BYTES (read COPY_BYTES, write COPY_BYTES) per launch."""
+    import torch
+    src = torch.randn(COPY_BYTES // 4, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES, "launches": steps}))
+
+
+def _pmc_kib_per_dispatch(directory: str, counter: str, kernel_substr: str) -> float:
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]:
+                vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {counter} rows for '{kernel_substr}' under {directory}")
+    return statistics.median(vals.values())
+
+
+def traffic_summary(attn_fetch, attn_write, copy_fetch, copy_write, workload, causal):
+    """HBM bytes per attention launch: FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by
+    the ratio of known bytes to what the same counter reads for the plain copy kernel."""
+    f_copy = _pmc_kib_per_dispatch(copy_fetch, "FETCH_SIZE", "elementwise") * 1024
+    w_copy = _pmc_kib_per_dispatch(copy_write, "WRITE_SIZE", "elementwise") * 1024
+    f_attn = _pmc_kib_per_dispatch(attn_fetch, "FETCH_SIZE", "attn_fwd_kernel") * 1024
+    w_attn = _pmc_kib_per_dispatch(attn_write, "WRITE_SIZE", "attn_fwd_kernel") * 1024
+    f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
+    entry = {"bytes_per_launch": round(f_attn * f_scale + w_attn * w_scale),
+             "read_bytes": round(f_attn * f_scale), "written_bytes": round(w_attn * w_scale),
+             "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+             "raw_fetch_kib": f_attn / 1024, "raw_write_kib": w_attn / 1024,
+             "source_sha256_16": source_hash()}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        table = {}
+    table[f"{workload}-causal{causal}"] = entry
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+    print(json.dumps({f"{workload}-causal{causal}": entry}))
 
 
 def cpu_baseline(w, causal, q, k, v, out, lse, budget_s: float):
@@ -97,13 +153,25 @@ def main():
     ap.add_argument("--causal", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--traffic-summary", nargs=4, metavar="DIR")
     args = ap.parse_args()
+
+    if args.traffic_summary:
+        import attn_workloads as aw
+        w = aw.by_name(args.workload) if args.workload else aw.WORKLOADS[aw.HEADLINE]
+        traffic_summary(*args.traffic_summary, w.name, w.causal_modes[0] if args.causal is None else args.causal)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(heads or query tiles would shard across GPUs with no exchange); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calibration:
+        copy_calibration(args.steps)
+        return
 
     import torch
     import attn_workloads as aw
