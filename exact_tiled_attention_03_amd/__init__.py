@@ -40,12 +40,23 @@ def load_library():
                              ctypes.c_int, ctypes.c_void_p]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [ctypes.c_int]
+    lib.attn_fwd_schedule.restype = ctypes.c_int
+    lib.attn_fwd_schedule.argtypes = [ctypes.c_int] * 5
     _lib = lib
     return lib
 
 
 def attn_status_string(status: int) -> str:
     return load_library().attn_status_string(int(status)).decode()
+
+
+ATTN_SCHEDULE_SMALL = 0
+ATTN_SCHEDULE_WIDE = 1
+
+
+def attn_fwd_schedule(B: int, H: int, N: int, d: int, causal: bool) -> int:
+    """Kernel schedule attn_fwd uses for this shape (negative status if rejected)."""
+    return load_library().attn_fwd_schedule(int(B), int(H), int(N), int(d), int(bool(causal)))
 
 
 def _dtype_code(t):
@@ -105,4 +116,5 @@ def attention(q, k, v, causal: bool, scale: float, stream=None):
     return out, lse
 
 
-__all__ = ["attn_fwd", "attn_status_string", "attention", "load_library", "AttnError", "ATTN_F16", "ATTN_BF16"]
+__all__ = ["attn_fwd", "attn_fwd_schedule", "attn_status_string", "attention", "load_library", "AttnError",
+           "ATTN_F16", "ATTN_BF16", "ATTN_SCHEDULE_SMALL", "ATTN_SCHEDULE_WIDE"]

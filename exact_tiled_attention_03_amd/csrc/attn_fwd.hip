@@ -1,41 +1,44 @@
 // attn_fwd.hip -- fused exact-attention forward for gfx950 (MI355X) and its C ABI.
 //
 // Method: "Triton in depth: from matmul to Flash Attention" (ybb.press),
-// sections 3.2-3.3.  Each work-group owns one query tile of one (batch, head)
-// and walks the key/value tiles once, keeping for every query row the running
-// max m and running sum l of the exponentials; the fp32 output accumulator is
-// rescaled by exp(m_old - m_new) whenever the max grows, and divided by l once
-// after the loop.  Keys with index > query index are excluded when causal.
-// The N x N score matrix never leaves registers.
+// sections 3.2-3.3.  A work-group owns query tiles of one (batch, head) and
+// walks the key/value tiles once, keeping for every query row the running max
+// m and running sum l of the exponentials; the fp32 output accumulator is
+// rescaled by exp(m_old - m_new) when the max grows and divided by l once after
+// the loop.  Keys with index > query index are excluded when causal.  The
+// N x N score matrix never leaves registers.
 //
 // gfx950 mapping (not taken from the pages, which target NVIDIA tensor cores):
 //
 //  * Scores are produced transposed, S^T = K Q^T, with v_mfma_f32_32x32x16.
 //    In the 32x32 accumulator layout a lane owns one column, so each lane
-//    holds 16 scores of ONE query.  The row max is then 15 lane-local max ops
-//    plus one exchange with lane^32 (the other half of the same column); the
-//    row sum needs no exchange until the epilogue.
+//    holds 16 scores of ONE query.  The row max is 15 lane-local max ops plus
+//    one exchange with lane^32 (the other half of the same column); the row
+//    sum needs no exchange until the epilogue.
 //  * The K rows fed to the A operand are permuted (kperm) so that the 16
 //    accumulator registers of a lane map to two runs of 8 consecutive keys.
-//    Those runs are exactly the B operand layout of the next MFMA,
-//    O^T += V^T P^T, so P goes from the score accumulator to the P.V operand
-//    without leaving the lane.
-//  * V^T is needed as an A operand with 8 consecutive keys per lane; the
-//    loader transposes 4x8 blocks in registers and stores V^T in LDS.
-//  * K and V^T tiles are double-buffered in LDS with one-chunk row padding,
-//    which makes the 16-byte operand reads bank-conflict free.
-//  * Work-groups are remapped so that consecutive ids on one XCD (ids are
-//    dealt round-robin over the 8 XCDs) cover the query tiles of the same
-//    heads: a head's K/V then stays in that XCD's L2.  Causal tiles run
-//    longest first to shorten the tail.
+//    Those runs are exactly the B operand layout of O^T += V^T P^T, so P goes
+//    from the score accumulator to the P.V operand without leaving the lane.
+//  * K and V tiles go from HBM straight into LDS (buffer loads with the LDS
+//    destination), double-buffered, rows XOR-swizzled for conflict-free reads.
+//    V stays row-major; its P.V operand is read with the gfx950 transpose load.
+//  * Work-groups are remapped so that each XCD (ids are dealt round-robin over
+//    the 8 XCDs) gets a contiguous run of heads, keeping a head's K/V in one
+//    L2.  A causal work-group takes the query-tile pair (i, nqt-1-i), so all
+//    work-groups do the same amount of work.
 //  * exp is evaluated as exp2 with scale*log2(e) folded into one FMA; lse is
 //    returned in natural-log units.
+//
+// Waves run free (no phase coupling): two work-groups share a CU, so on each
+// SIMD one wave's exponentials overlap the other's MFMAs.  Large problems use
+// 8 waves (256 queries) per work-group, halving the K/V loads per query; small
+// ones use 4 waves (128 queries) so that the grid still fills the 256 CUs.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
-#include <cfloat>
 #include <cstring>
 #include <type_traits>
 
@@ -51,15 +54,9 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
-// Compile-time tuning knobs (defaults are the shipped configuration).
-#ifndef ETA_WAVES_PER_EU
-#define ETA_WAVES_PER_EU 2      // waves per SIMD the register budget is sized for
-#endif
+// log2 headroom before the reference max is raised (see Wave::prepare)
 #ifndef ETA_RESCALE_TH
-#define ETA_RESCALE_TH 8.0f     // log2 headroom before the running max is raised
-#endif
-#ifndef ETA_LANE_SWAP
-#define ETA_LANE_SWAP 1         // 1: v_permlane32_swap for the lane-pair exchange, 0: ds_bpermute
+#define ETA_RESCALE_TH 8.0f
 #endif
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -105,27 +102,21 @@ struct FwdArgs {
     int N;
     int BH;
     int nqt;           // query tiles per head
-    float c;           // |scale| * log2(e)
+    int ngroups;       // work-groups per head: causal pairs tiles (i, nqt-1-i), else nqt
+    float c;           // |scale| * log2(e), > 0
     unsigned qsign;    // 0x80008000 when scale < 0 (Q negated exactly), else 0
 };
 
-// Value of x in the lane 32 positions away (the other half of the same accumulator column).
+// x combined with the value in the lane 32 positions away (the other half of
+// the same accumulator column), through v_permlane32_swap.
 __device__ __forceinline__ float pair_max(float x) {
-#if ETA_LANE_SWAP
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-#else
-    return fmaxf(x, __shfl_xor(x, 32));
-#endif
 }
 
 __device__ __forceinline__ float pair_sum(float x) {
-#if ETA_LANE_SWAP
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-#else
-    return x + __shfl_xor(x, 32);
-#endif
 }
 
 // Row of the K tile that feeds A-operand row m of the score MFMA.  With this
@@ -135,7 +126,7 @@ __device__ __forceinline__ int kperm(int m) {
     return 16 * (m >> 4) + 8 * ((m >> 2) & 1) + 4 * ((m >> 3) & 1) + (m & 3);
 }
 
-// Tile configuration shared by the kernel and the host launcher.
+// Tile configuration shared by the kernels and the host launcher.
 //
 // LDS holds two stages of K and V, each a BN x ROWB byte array written by
 // direct global->LDS loads: one load instruction of a wave fills 1 KB of
@@ -146,14 +137,16 @@ __device__ __forceinline__ int kperm(int m) {
 //    same logical chunk: chunk c of row r sits at c ^ kswz(r), kswz(r) =
 //    (r / RPB) % CPRP with RPB rows per 256-byte bank line.
 //  * V is read by 8-byte transpose loads, 4 consecutive rows x one 64-byte
-//    granule per 32 lanes: the granule index g of row r sits at
-//    g ^ ((r / RPB) % GPR), GPR granules per row.
-template <int D> struct Cfg {
-    static constexpr int WAVES = 4;
+//    granule per 32 lanes: the granule index g of row r sits at g ^ vswz(r),
+//    vswz(r) = (r / RPB) % GPR with GPR granules per row.  It only moves whole
+//    granules, so rows 4 apart differ by a fixed offset for every lane.
+template <int D, int WAVES_> struct Cfg {
+    static constexpr int WAVES = WAVES_;
     static constexpr int NT = 64 * WAVES;             // threads per work-group
     static constexpr int BM = 32 * WAVES;             // queries per work-group (32 per wave)
     static constexpr int BN = 64;                     // keys per tile
     static constexpr int SB = BN / 32;                // 32-key score blocks per tile
+    static constexpr int KK = BN / 16;                // 16-key P.V k-steps per tile
     static constexpr int KSTEPS = D / 16;             // MFMA k-steps over the head dim
     static constexpr int DBLK = (D + 31) / 32;        // 32-row blocks of O^T
     static constexpr int CPR = D / 8;                 // 16-byte chunks per row in HBM
@@ -166,8 +159,10 @@ template <int D> struct Cfg {
     static constexpr int VOFF = 2 * TILEB;            // V stage s at VOFF + s * TILEB
     static constexpr int LDS = 4 * TILEB;
     static constexpr int IT = TILEB / (16 * NT);      // direct-load instructions per tile and thread
+    static __device__ __forceinline__ int kswz(int r) { return (r / RPB) % CPRP; }
+    static __device__ __forceinline__ int vswz(int r) { return (r / RPB) % GPR; }
     static_assert(D % 16 == 0 && CPR <= CPRP, "head dim");
-    static_assert(TILEB % (16 * NT) == 0, "a tile is a whole number of load rounds");
+    static_assert(IT >= 1 && TILEB % (16 * NT) == 0, "a tile is a whole number of load rounds");
     static_assert(DBLK <= GPR, "transpose reads of the padded head dim stay inside a row");
     static_assert(VOFF + 2 * TILEB <= 65536, "LDS offsets fit the 16-bit immediate");
 };
@@ -188,121 +183,140 @@ __device__ __forceinline__ u32x4_t lds_read16(unsigned addr) {
     return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>((lds_bytes)(size_t)addr);
 }
 
-template <int D, int DT, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ETA_WAVES_PER_EU, ETA_WAVES_PER_EU)))
-void attn_fwd_kernel(FwdArgs a) {
-#if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
-    using C = Cfg<D>;
-    using E = Elem<DT>;
-    constexpr int BN = C::BN, SB = C::SB, KSTEPS = C::KSTEPS, DBLK = C::DBLK, CPR = C::CPR;
-    constexpr int CPRP = C::CPRP, ROWB = C::ROWB;
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS];
-    const unsigned lds0 = (unsigned)(size_t)(lds_bytes)smem;
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    const int hf = lane >> 5;   // which half of the 64-lane wave
-    const int n = lane & 31;    // accumulator column = query within the wave's 32
+#if defined(__HIP_DEVICE_COMPILE__)
 
-    // ---- work-group -> (head, query tile): XCD-aware, causal longest first
-    const int T = a.nqt * a.BH;
+// Work-group id -> (head, group): ids are dealt round-robin over the 8 XCDs,
+// so XCD x runs ids x, x+8, ...; the remap gives each XCD a contiguous range
+// of (head, group) indices.
+__device__ __forceinline__ void map_workgroup(const FwdArgs& a, int& bh, int& grp) {
+    const int T = a.ngroups * a.BH;
     const int L = blockIdx.x;
     const int xcd = L & 7;
     const int vidx = xcd * (T >> 3) + min(xcd, T & 7) + (L >> 3);
-    const int bh = vidx / a.nqt;
-    int qt = vidx - bh * a.nqt;
-    if (CAUSAL) qt = a.nqt - 1 - qt;
+    bh = vidx / a.ngroups;
+    grp = vidx - bh * a.ngroups;
+}
 
-    const int N = a.N;
-    const int q0 = qt * C::BM;
-    const int qw0 = q0 + wave * 32;
-    const int qi = qw0 + n;
-    const size_t hoff = (size_t)bh * (size_t)N * CPR;   // head offset in 16-byte chunks
+// State and arithmetic of one wave: 32 query rows (one per accumulator column;
+// the two lanes of a column each hold half of the keys of a tile).
+template <int D, int DT, bool CAUSAL, int WAVES>
+struct Wave {
+    using C = Cfg<D, WAVES>;
+    using E = Elem<DT>;
+    static constexpr int SB = C::SB, KK = C::KK, KSTEPS = C::KSTEPS, DBLK = C::DBLK, CPR = C::CPR;
 
-    // ---- Q fragments (B operand of S^T = K Q^T), loaded once
-    u32x4_t qf[KSTEPS];
-    if (qi < N) {
-        const u32x4_t* src = a.q + hoff + (size_t)qi * CPR + hf;
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = src[2 * ks] ^ a.qsign;
-    } else {
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = u32x4_t{0, 0, 0, 0};
-    }
+    int lane, wave, hf, n, N, qw0, qi;
+    float c;
+    unsigned lds0;
+    const unsigned char* kbase;
+    const unsigned char* vbase;
+    unsigned kvo[C::IT], vvo[C::IT];   // per-lane offsets of the direct loads
+    unsigned ka[KSTEPS];               // per-lane LDS addresses of the score A operand
+    unsigned va[DBLK];                 // per-lane LDS addresses of the P.V A operand
+    u32x4_t qf[KSTEPS];                // Q^T fragments (score B operand)
+    f32x16_t o[DBLK];                  // O^T accumulator
+    float m, l;                        // reference max (log2 units) and this half's sum
 
-    const int kend = CAUSAL ? min(N, q0 + C::BM) : N;
-    const int nt = (kend + BN - 1) / BN;
-
-    // ---- direct global -> LDS loads.  Slot (it, wave, lane) of a tile holds
-    // row r = slot / CPRP, physical chunk p = slot % CPRP, i.e. logical chunk
-    // p ^ swizzle(r); chunks past the head dim get an out-of-range offset and
-    // read as zero, as do rows past N (the buffer ends at row N).
-    unsigned kvo[C::IT], vvo[C::IT];
-#pragma unroll
-    for (int it = 0; it < C::IT; ++it) {
-        const int slot = it * C::NT + wave * 64 + lane;
-        const int r = slot / CPRP, p = slot % CPRP;
-        const int kc = p ^ ((r / C::RPB) % CPRP);
-        const int vc = p ^ (4 * ((r / C::RPB) % C::GPR));
-        kvo[it] = kc < CPR ? (unsigned)(r * D * 2 + kc * 16) : 0x80000000u;
-        vvo[it] = vc < CPR ? (unsigned)(r * D * 2 + vc * 16) : 0x80000000u;
-    }
-    const unsigned char* kbase = reinterpret_cast<const unsigned char*>(a.k + hoff);
-    const unsigned char* vbase = reinterpret_cast<const unsigned char*>(a.v + hoff);
-    auto issue_loads = [&](int j, int stage) {
-        const int kt0 = j * BN;
-        const int bytes = (N - kt0) * D * 2;            // rows kt0 .. N-1 are in range
-        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + (size_t)kt0 * D * 2), 0, bytes, 0x00020000);
-        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + (size_t)kt0 * D * 2), 0, bytes, 0x00020000);
+    __device__ __forceinline__ void init(const FwdArgs& a, unsigned lds_base, int tid, int wave_) {
+        lane = tid & 63;
+        wave = wave_;
+        hf = lane >> 5;
+        n = lane & 31;
+        N = a.N;
+        c = a.c;
+        lds0 = lds_base;
+        // direct-load slot (it, wave, lane) of a tile holds row r = slot / CPRP,
+        // physical chunk p = slot % CPRP, i.e. logical chunk p ^ swizzle(r); chunks
+        // past the head dim get an out-of-range offset and read as zero, as do rows
+        // past N (the buffer ends at row N)
 #pragma unroll
         for (int it = 0; it < C::IT; ++it) {
-            const unsigned dst = (unsigned)((it * C::NT + wave * 64) * 16);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void*)(lds_bytes)(size_t)(lds0 + C::KOFF + stage * C::TILEB + dst), 16, kvo[it], 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(lds_bytes)(size_t)(lds0 + C::VOFF + stage * C::TILEB + dst), 16, vvo[it], 0, 0, 0);
+            const int slot = slot_base(it) + lane;
+            const int r = slot / C::CPRP, p = slot % C::CPRP;
+            const int kc = p ^ C::kswz(r);
+            const int vc = p ^ (4 * C::vswz(r));
+            kvo[it] = kc < CPR ? (unsigned)(r * D * 2 + kc * 16) : 0x80000000u;
+            vvo[it] = vc < CPR ? (unsigned)(r * D * 2 + vc * 16) : 0x80000000u;
         }
-    };
-
-    // ---- per-lane LDS read addresses (stage 0; stage 1 adds TILEB)
-    unsigned ka[KSTEPS];   // score A operand: row kperm(n), logical chunk 2*ks + hf
-    {
-        const int r = kperm(n);
-        const int x = (r / C::RPB) % CPRP;
+        {
+            const int r = kperm(n);
+            const int x = C::kswz(r);                              // rows r and r + 32 share it
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) ka[ks] = lds0 + C::KOFF + r * ROWB + (((2 * ks + hf) ^ x) * 16);
-    }
-    unsigned va[DBLK];     // P.V A operand via transpose reads (see lds_read_tr)
-    {
-        const int g16 = lane >> 4, s16 = lane & 15;
-        const int r = 8 * (g16 >> 1) + (s16 >> 2);           // + 16*kk + 4*half, both multiples of 4
-        const int x = (r / C::RPB) % C::GPR;
+            for (int ks = 0; ks < KSTEPS; ++ks) ka[ks] = lds0 + C::KOFF + r * C::ROWB + (((2 * ks + hf) ^ x) * 16);
+        }
+        {
+            const int g16 = lane >> 4, s16 = lane & 15;
+            const int r = 8 * (g16 >> 1) + (s16 >> 2);           // + 16*kk + 4*half: multiples of 4 rows
+            const int x = C::vswz(r);                             // the same for r + 16*kk + 4*half
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db)
-            va[db] = lds0 + C::VOFF + r * ROWB + (4 * (db ^ x) + 2 * (g16 & 1) + ((s16 & 3) >> 1)) * 16 + 8 * (s16 & 1);
+            for (int db = 0; db < DBLK; ++db)
+                va[db] = lds0 + C::VOFF + r * C::ROWB + (4 * (db ^ x) + 2 * (g16 & 1) + ((s16 & 3) >> 1)) * 16 + 8 * (s16 & 1);
+        }
     }
 
-    // ---- per-lane running state (one query row per lane, half the keys)
-    f32x16_t o[DBLK];
+    // start a query tile: this wave's rows begin at qw0_
+    __device__ __forceinline__ void begin(const FwdArgs& a, int bh, int qw0_) {
+        qw0 = qw0_;
+        qi = qw0 + n;
+        const size_t hoff = (size_t)bh * (size_t)N * CPR;   // head offset in 16-byte chunks
+        kbase = reinterpret_cast<const unsigned char*>(a.k + hoff);
+        vbase = reinterpret_cast<const unsigned char*>(a.v + hoff);
+        if (qi < N) {
+            const u32x4_t* src = a.q + hoff + (size_t)qi * CPR + hf;
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) o[db] = f32x16_t{};
-    float m = kNegInf;   // reference max of scale*log2(e)*score, shared by both halves
-    float l = 0.f;       // sum over this half's keys of exp2(t - m)
-    const float c = a.c;
+            for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = src[2 * ks] ^ a.qsign;
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = u32x4_t{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) o[db] = f32x16_t{};
+        m = kNegInf;
+        l = 0.f;
+    }
 
-    // One K/V tile for this wave; need_mask (wave-uniform) on diagonal/ragged tiles.
-    auto tile = [&](auto stage_tag, bool need_mask, int kt0) {
-        constexpr int ST = decltype(stage_tag)::value * C::TILEB;
-        // S^T = K Q^T: two independent 32-key accumulators, interleaved
-        f32x16_t s[SB];
+    // this wave's share of tile j of K (is_v false) or V into LDS stage `stage`
+    __device__ __forceinline__ void issue(bool is_v, int j, int stage) const {
+        const int kt0 = j * C::BN;
+        const int bytes = (N - kt0) * D * 2;            // rows kt0 .. N-1 are in range
+        const unsigned char* base = (is_v ? vbase : kbase) + (size_t)kt0 * D * 2;
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, 0x00020000);
+        const unsigned region = lds0 + (is_v ? C::VOFF : C::KOFF) + stage * C::TILEB;
+#pragma unroll
+        for (int it = 0; it < C::IT; ++it) {
+            const unsigned dst = region + (unsigned)(slot_base(it) * 16);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_bytes)(size_t)dst, 16,
+                                                     is_v ? vvo[it] : kvo[it], 0, 0, 0);
+        }
+    }
+
+    // first slot of load round `it` for this wave
+    __device__ __forceinline__ int slot_base(int it) const { return (it * C::WAVES + wave) * 64; }
+
+    // does this wave have keys to process in tile j?
+    __device__ __forceinline__ bool active(int j) const { return qw0 < N && (!CAUSAL || j * C::BN <= qw0 + 31); }
+
+    // S^T = K Q^T for the tile in K stage ST: two independent 32-key accumulators
+    template <int ST>
+    __device__ __forceinline__ void score(f32x16_t (&s)[SB]) const {
 #pragma unroll
         for (int sb = 0; sb < SB; ++sb) s[sb] = f32x16_t{};
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
             for (int sb = 0; sb < SB; ++sb)
-                s[sb] = E::mfma(lds_read16(ka[ks] + ST + sb * 32 * ROWB), qf[ks], s[sb]);
+                s[sb] = E::mfma(lds_read16(ka[ks] + ST * C::TILEB + sb * 32 * C::ROWB), qf[ks], s[sb]);
+    }
 
-        if (need_mask) {
+    // Mask tile j's scores where needed and update the reference max.  m is
+    // raised only when a tile's max exceeds it by more than ETA_RESCALE_TH (log2
+    // units), so p <= 2^TH and the O rescale is rare; m, l and O always refer to
+    // the same m, so the result is unchanged.
+    __device__ __forceinline__ void prepare(f32x16_t (&s)[SB], int j) {
+        const int kt0 = j * C::BN;
+        if ((CAUSAL && kt0 + C::BN - 1 > qw0) || kt0 + C::BN > N) {
             // key index of register i is kt0 + 8*hf + 32*sb + 16*(i/8) + i%8; it is
             // kept iff that is <= lim (the query for causal, N-1 for the tail)
             const int lim = (CAUSAL ? min(qi, N - 1) : N - 1) - (kt0 + 8 * hf);
@@ -312,10 +326,6 @@ void attn_fwd_kernel(FwdArgs a) {
                 for (int i = 0; i < 16; ++i)
                     if (32 * sb + 16 * (i >> 3) + (i & 7) > lim) s[sb][i] = kNegInf;
         }
-
-        // online softmax.  m is raised only when a tile's max exceeds it by more
-        // than ETA_RESCALE_TH (log2 units), so p <= 2^TH and the O rescale is rare;
-        // m, l and O always refer to the same m, so the result is unchanged.
         float mx = kNegInf;
 #pragma unroll
         for (int sb = 0; sb < SB; ++sb)
@@ -323,93 +333,159 @@ void attn_fwd_kernel(FwdArgs a) {
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
         const float mt = pair_max(mx) * c;           // c > 0, so -inf stays -inf
         const bool grow = mt > m + ETA_RESCALE_TH;
-        const float mnew = grow ? mt : m;
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;   // 0 when m was -inf
-        m = mnew;
-        const float nm = m > kNegInf ? -m : 0.f;
-
-        u32x4_t pf[2 * SB];   // P^T as B operands of the P.V k-steps (16 keys each)
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int sb = 0; sb < SB; ++sb) {
-            float p[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][i], c, nm));
-                part[i & 3] += p[i];
-            }
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-                pf[2 * sb + hh] = u32x4_t{E::pack2(p[8 * hh + 0], p[8 * hh + 1]), E::pack2(p[8 * hh + 2], p[8 * hh + 3]),
-                                          E::pack2(p[8 * hh + 4], p[8 * hh + 5]), E::pack2(p[8 * hh + 6], p[8 * hh + 7])};
-        }
-        l = l * alpha + ((part[0] + part[1]) + (part[2] + part[3]));
-
         if (__any(grow)) {
+            const float mnew = grow ? mt : m;
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;   // 0 when m was -inf
+            m = mnew;
+            l *= alpha;
 #pragma unroll
             for (int db = 0; db < DBLK; ++db) o[db] *= alpha;
         }
-        // O^T += V^T P^T; V^T operand = two transpose reads of 4 keys each
-#pragma unroll
-        for (int kk = 0; kk < 2 * SB; ++kk)
-#pragma unroll
-            for (int db = 0; db < DBLK; ++db) {
-                const u32x2_t lo = lds_read_tr(va[db] + ST + 16 * kk * ROWB);
-                const u32x2_t hi = lds_read_tr(va[db] + ST + (16 * kk + 4) * ROWB);
-                o[db] = E::mfma(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pf[kk], o[db]);
-            }
-    };
-
-    // one loop step: prefetch tile j+1 into the other stage, compute tile j, sync
-    auto step = [&](auto stage_tag, int j) {
-        constexpr int STAGE = decltype(stage_tag)::value;
-        if (j + 1 < nt) issue_loads(j + 1, STAGE ^ 1);
-        const int kt0 = j * BN;
-        // tiles wholly above this wave's diagonal, or waves past N, do no math
-        if (qw0 < N && (!CAUSAL || kt0 <= qw0 + 31))
-            tile(stage_tag, (CAUSAL && kt0 + BN - 1 > qw0) || kt0 + BN > N, kt0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-    };
-
-    issue_loads(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    for (int j = 0; j < nt; j += 2) {
-        step(std::integral_constant<int, 0>{}, j);
-        if (j + 1 < nt) step(std::integral_constant<int, 1>{}, j + 1);
     }
 
-    // ---- epilogue: O = acc / l, lse = ln2 * (m + log2 l)
-    if (qw0 < N) {
-        const float ltot = pair_sum(l);
-        if (qi < N) {
-            const float inv = 1.0f / ltot;
-            uint16_t* orow = a.o + ((size_t)bh * N + qi) * D;
+    // P = exp2(c*s - m), rounded to the input type and packed as the B operands
+    // of the P.V k-steps; the fp32 probabilities are added to l
+    __device__ __forceinline__ void probs(const f32x16_t (&s)[SB], u32x4_t (&pf)[KK]) {
+        const float nm = m > kNegInf ? -m : 0.f;
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int db = 0; db < DBLK; ++db)
+        for (int kk = 0; kk < KK; ++kk) {
+            float p[8];
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int d0 = db * 32 + 8 * g + 4 * hf;
-                    if (d0 < D) {
-                        const u32x2_t w = {E::pack2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv),
-                                           E::pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
-                        *reinterpret_cast<u32x2_t*>(orow + d0) = w;
-                    }
-                }
-            if (a.lse != nullptr && hf == 0) a.lse[(size_t)bh * N + qi] = (m + __builtin_amdgcn_logf(ltot)) * kLn2;
+            for (int i = 0; i < 8; ++i) {
+                p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kk >> 1][8 * (kk & 1) + i], c, nm));
+                part[i & 3] += p[i];
+            }
+            pf[kk] = u32x4_t{E::pack2(p[0], p[1]), E::pack2(p[2], p[3]), E::pack2(p[4], p[5]), E::pack2(p[6], p[7])};
         }
+        l += (part[0] + part[1]) + (part[2] + part[3]);
+    }
+
+    // O^T += V^T P^T for the tile in V stage ST; V^T operand = two transpose
+    // reads of 4 keys each
+    template <int ST>
+    __device__ __forceinline__ void pv(const u32x4_t (&pf)[KK]) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) {
+                const u32x2_t lo = lds_read_tr(va[db] + ST * C::TILEB + 16 * kk * C::ROWB);
+                const u32x2_t hi = lds_read_tr(va[db] + ST * C::TILEB + (16 * kk + 4) * C::ROWB);
+                o[db] = E::mfma(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pf[kk], o[db]);
+            }
+    }
+
+    // O = acc / l rounded to the input type; lse = ln2 * (m + log2 l)
+    __device__ __forceinline__ void finish(const FwdArgs& a, int bh) {
+        if (qw0 >= N) return;
+        const float ltot = pair_sum(l);
+        if (qi >= N) return;
+        const float inv = 1.0f / ltot;
+        uint16_t* orow = a.o + ((size_t)bh * N + qi) * D;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = db * 32 + 8 * g + 4 * hf;
+                if (d0 < D) {
+                    const u32x2_t w = {E::pack2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv),
+                                       E::pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+                    *reinterpret_cast<u32x2_t*>(orow + d0) = w;
+                }
+            }
+        if (a.lse != nullptr && hf == 0) a.lse[(size_t)bh * N + qi] = (m + __builtin_amdgcn_logf(ltot)) * kLn2;
+    }
+};
+
+#endif  // __HIP_DEVICE_COMPILE__
+
+// ---- the kernel: WAVES free-running waves per work-group ---------------------
+template <int D, int DT, bool CAUSAL, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_kernel(FwdArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
+    using C = Cfg<D, WAVES>;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS];
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    Wave<D, DT, CAUSAL, WAVES> w;
+    w.init(a, (unsigned)(size_t)(lds_bytes)smem, tid, wave);
+
+    int bh, grp;
+    map_workgroup(a, bh, grp);
+    const int nitems = CAUSAL && grp != a.nqt - 1 - grp ? 2 : 1;
+    for (int item = 0; item < nitems; ++item) {
+        const int qt = CAUSAL ? (item == 0 ? a.nqt - 1 - grp : grp) : grp;
+        const int q0 = qt * C::BM;
+        w.begin(a, bh, q0 + 32 * wave);
+        const int kend = CAUSAL ? min(a.N, q0 + C::BM) : a.N;
+        const int nt = (kend + C::BN - 1) / C::BN;
+
+        // one step: prefetch tile j+1 into the other stage, compute tile j, sync.
+        // The wave raises its priority while it issues the score MFMAs, so the
+        // matrix pipe is fed as soon as it frees up while the other wave on the
+        // SIMD works through its exponentials.
+        auto step = [&](auto stage_tag, int j) {
+            constexpr int ST = decltype(stage_tag)::value;
+            if (j + 1 < nt) {
+                w.issue(false, j + 1, ST ^ 1);
+                w.issue(true, j + 1, ST ^ 1);
+            }
+            if (w.active(j)) {
+                f32x16_t s[C::SB];
+                u32x4_t pf[C::KK];
+                __builtin_amdgcn_s_setprio(2);
+                w.template score<ST>(s);
+                __builtin_amdgcn_s_setprio(0);
+                w.prepare(s, j);
+                w.probs(s, pf);
+                w.template pv<ST>(pf);
+            }
+            wait_loads();
+            __syncthreads();
+        };
+        w.issue(false, 0, 0);
+        w.issue(true, 0, 0);
+        wait_loads();
+        __syncthreads();
+        for (int j = 0; j < nt; j += 2) {
+            step(std::integral_constant<int, 0>{}, j);
+            if (j + 1 < nt) step(std::integral_constant<int, 1>{}, j + 1);
+        }
+        w.finish(a, bh);
     }
 #endif
 }
 
 // --- host side ---------------------------------------------------------------
 
-template <int D, int DT, bool CAUSAL>
-hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-    const unsigned grid = (unsigned)a.nqt * (unsigned)a.BH;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, CAUSAL>), dim3(grid), dim3(Cfg<D>::NT), 0, stream, a);
+// Work-groups of 256 queries needed before the 8-wave kernel is used: below
+// about two rounds of the 256 CUs (one such work-group fits per CU) the
+// 128-query work-groups fill the chip better.
+#ifndef ETA_WIDE_MIN_GROUPS
+#define ETA_WIDE_MIN_GROUPS 512
+#endif
+constexpr long long kWideMinGroups = ETA_WIDE_MIN_GROUPS;
+
+bool use_wide(long long bh, long long N, int causal) {
+    const long long nqt = (N + 255) / 256;
+    return (causal ? (nqt + 1) / 2 : nqt) * bh >= kWideMinGroups;
+}
+
+template <int D, int DT, bool CAUSAL, int WAVES>
+hipError_t launch_waves(FwdArgs a, hipStream_t stream) {
+    constexpr int BM = Cfg<D, WAVES>::BM;
+    const long long nqt = ((long long)a.N + BM - 1) / BM;
+    a.nqt = (int)nqt;
+    a.ngroups = CAUSAL ? (int)((nqt + 1) / 2) : (int)nqt;
+    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, CAUSAL, WAVES>), dim3((unsigned)a.ngroups * (unsigned)a.BH),
+                       dim3(64 * WAVES), 0, stream, a);
     return hipGetLastError();
+}
+
+template <int D, int DT, bool CAUSAL>
+hipError_t launch(FwdArgs a, hipStream_t stream) {
+    return use_wide(a.BH, a.N, CAUSAL) ? launch_waves<D, DT, CAUSAL, 8>(a, stream) : launch_waves<D, DT, CAUSAL, 4>(a, stream);
 }
 
 template <int D, int DT>
@@ -440,6 +516,18 @@ int check_device() {
     return ok ? ATTN_OK : ATTN_ERR_DEVICE;
 }
 
+// shape checks shared by attn_fwd and attn_fwd_schedule
+int check_shape(int B, int H, int N, int d, int causal) {
+    if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
+    if (d != 64 && d != 80 && d != 128) return ATTN_ERR_HEAD_DIM;
+    if (causal != 0 && causal != 1) return ATTN_ERR_CAUSAL;
+    const long long bh = (long long)B * H;
+    const long long nqt = ((long long)N + 127) / 128;   // the smaller query tile bounds the grid
+    if (bh > INT32_MAX || nqt * bh > INT32_MAX) return ATTN_ERR_SHAPE;
+    if ((long long)N * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;   // one head must fit a 32-bit buffer range
+    return ATTN_OK;
+}
+
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
     return x < y + nb && y < x + na;
@@ -457,14 +545,11 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
     if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15u) return ATTN_ERR_ALIGN;
     if ((uintptr_t)lse & 3u) return ATTN_ERR_ALIGN;
+    const int shape_status = check_shape(B, H, N, d, causal);
+    if (shape_status != ATTN_OK) return shape_status;
 
     const long long bh = (long long)B * H;
-    const int bm = Cfg<128>::BM;   // the same for every head dim
-    const long long nqt = ((long long)N + bm - 1) / bm;
-    if (bh > INT32_MAX || nqt * bh > INT32_MAX) return ATTN_ERR_SHAPE;
-    if ((long long)N * d * 2 > INT32_MAX) return ATTN_ERR_SHAPE;   // one head must fit a 32-bit buffer range
     const size_t tensor_bytes = (size_t)bh * (size_t)N * (size_t)d * 2u;
-    if ((size_t)bh * (size_t)N * (size_t)d > (size_t)INT64_MAX / 4) return ATTN_ERR_SHAPE;
     const size_t lse_bytes = (size_t)bh * (size_t)N * 4u;
     if (overlaps(out, tensor_bytes, q, tensor_bytes) || overlaps(out, tensor_bytes, k, tensor_bytes) ||
         overlaps(out, tensor_bytes, v, tensor_bytes))
@@ -484,7 +569,8 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
     a.lse = lse;
     a.N = N;
     a.BH = (int)bh;
-    a.nqt = (int)nqt;
+    a.nqt = 0;       // set per kernel by launch()
+    a.ngroups = 0;
     // c must be > 0 so that masked scores (-inf) map to -inf; scale == 0 uses the
     // smallest normal float, which makes every exponent round to exactly 0
     a.c = scale == 0.f ? FLT_MIN : std::fabs(scale) * kLog2e;
@@ -500,11 +586,17 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
     return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
+extern "C" int attn_fwd_schedule(int B, int H, int N, int d, int causal) {
+    const int st = check_shape(B, H, N, d, causal);
+    if (st != ATTN_OK) return -st;
+    return use_wide((long long)B * H, N, causal) ? ATTN_SCHEDULE_WIDE : ATTN_SCHEDULE_SMALL;
+}
+
 extern "C" const char* attn_status_string(int status) {
     switch (status) {
         case ATTN_OK: return "success";
         case ATTN_ERR_NULL: return "q, k, v or out is NULL";
-        case ATTN_ERR_SHAPE: return "B, H and N must be >= 1 and the grid must fit in 2^31-1 work-groups";
+        case ATTN_ERR_SHAPE: return "B, H and N must be >= 1, the grid must fit in 2^31-1 work-groups and one head in 2 GB";
         case ATTN_ERR_HEAD_DIM: return "head dim must be 64, 80 or 128";
         case ATTN_ERR_DTYPE: return "dtype must be ATTN_F16 or ATTN_BF16";
         case ATTN_ERR_SCALE: return "scale must be finite";

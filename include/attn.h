@@ -37,7 +37,7 @@ typedef enum {
 typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,      /* q, k, v or out is NULL */
-    ATTN_ERR_SHAPE = 2,     /* B, H or N < 1, or the launch grid would exceed 2^31-1 work-groups */
+    ATTN_ERR_SHAPE = 2,     /* B, H or N < 1, the grid would exceed 2^31-1 work-groups, or N*d*2 > 2^31-1 bytes */
     ATTN_ERR_HEAD_DIM = 3,  /* d is not one of 64, 80, 128 */
     ATTN_ERR_DTYPE = 4,     /* dtype is not an attn_dtype value */
     ATTN_ERR_SCALE = 5,     /* scale is NaN or infinite */
@@ -85,6 +85,20 @@ typedef enum {
 int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              int B, int H, int N, int d, int causal, float scale, int dtype,
              void* stream);
+
+/*
+ * attn_fwd_schedule -- which kernel schedule attn_fwd uses for a shape.
+ *
+ * Returns ATTN_SCHEDULE_SMALL (4 waves, 128 queries per work-group, two
+ * work-groups per CU) or ATTN_SCHEDULE_WIDE (8 waves, 256 queries per
+ * work-group, one per CU), or a negative attn_status for arguments
+ * attn_fwd would reject by shape (ATTN_ERR_SHAPE, ATTN_ERR_HEAD_DIM,
+ * ATTN_ERR_CAUSAL).  Pure host function: no device is touched.  The choice
+ * depends on B*H, N and causal only; results do not depend on it beyond
+ * floating-point rounding order.
+ */
+typedef enum { ATTN_SCHEDULE_SMALL = 0, ATTN_SCHEDULE_WIDE = 1 } attn_schedule;
+int attn_fwd_schedule(int B, int H, int N, int d, int causal);
 
 /* Static, NUL-terminated English description of a status code (never NULL). */
 const char* attn_status_string(int status);

@@ -34,7 +34,7 @@ def declared_enum(name_prefix):
 
 
 def test_header_declares_entry_points():
-    assert declared_functions() == ["attn_fwd", "attn_status_string"]
+    assert declared_functions() == ["attn_fwd", "attn_fwd_schedule", "attn_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -88,6 +88,20 @@ def test_lse_may_be_null_then_device_is_checked(lib):
         pytest.skip("device check refuses only where no gfx950 is current")
     assert call(lib, lse=None) == 7
     assert call(lib) == 7
+
+
+def test_schedule_choice(lib):
+    import attn_workloads as aw
+    want = {"causal_b1_h1_n128_d64_fp16": 0, "causal_b4_h16_n1024_d64_fp16": 0,
+            "causal_b2_h32_n4096_d128_bf16": 1, "long_b1_h16_n32768_d128_bf16": 1, "ragged_b3_h8_n3000_d80_fp16": 0}
+    for w in aw.WORKLOADS:
+        for c in w.causal_modes:
+            assert eta.attn_fwd_schedule(w.B, w.H, w.N, w.d, c) == want[w.name], (w.name, c)
+    assert eta.attn_fwd_schedule(8, 64, 200, 80, 1) == 1      # 512 heads of one 256-query tile
+    assert eta.attn_fwd_schedule(8, 63, 200, 80, 1) == 0
+    assert eta.attn_fwd_schedule(1, 1, 8, 96, 0) == -3
+    assert eta.attn_fwd_schedule(0, 1, 8, 64, 0) == -2
+    assert lib.attn_fwd_schedule(1, 1, 8, 64, 3) == -9   # the binding itself coerces causal to 0/1
 
 
 def test_binding_rejects_cpu_tensors():

@@ -182,3 +182,37 @@ def test_rejects_misaligned_and_leaves_output(lib):
     assert ei.value.status == 6
     torch.cuda.synchronize()
     assert (big == 1.5).all()
+
+
+# Shapes with 512 heads select the 8-wave schedule even for short sequences,
+# so its masking, ragged tails and head dims are covered at small N.
+PP_N = [1, 65, 200, 256, 257, 300, 513]
+
+
+@pytest.mark.parametrize("d", [64, 80, 128])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_wide_schedule_edge_shapes(lib, d, dtype, causal):
+    for N in PP_N:
+        assert lib.attn_fwd_schedule(8, 64, N, d, causal) == lib.ATTN_SCHEDULE_WIDE
+        q, k, v = aw.make_inputs((8, 64, N, d), dtype, 9000 + N + d)
+        scale = 1.0 / math.sqrt(d)
+        out, lse = run_gpu(q, k, v, causal, scale)
+        assert_within_derived_bound(out, lse, q, k, v, causal, scale, label=f"wide N={N} d={d} {dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125])
+def test_wide_schedule_unusual_scales(lib, scale):
+    q, k, v = aw.make_inputs((8, 64, 130, 64), "bf16", 31)
+    for causal in (0, 1):
+        assert lib.attn_fwd_schedule(8, 64, 130, 64, causal) == lib.ATTN_SCHEDULE_WIDE
+        out, lse = run_gpu(q, k, v, causal, scale)
+        assert_within_derived_bound(out, lse, q, k, v, causal, scale, label=f"wide scale={scale} causal={causal}")
+
+
+def test_wide_schedule_long_causal_rows_and_outliers(lib):
+    q, k, v = aw.make_inputs((4, 128, 600, 128), "bf16", 32, outlier_fraction=0.02, outlier_factor=30.0)
+    assert lib.attn_fwd_schedule(4, 128, 600, 128, 1) == lib.ATTN_SCHEDULE_WIDE
+    out, lse = run_gpu(q, k, v, 1, 1 / math.sqrt(128))
+    assert_within_derived_bound(out, lse, q, k, v, 1, 1 / math.sqrt(128))
+    assert torch.equal(out[:, :, 0].view(torch.int16), v[:, :, 0].view(torch.int16))
