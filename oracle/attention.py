@@ -20,6 +20,17 @@ statistics (m, l) yields the exact result without storing the N x N matrix;
     O_i    = (sum_j P[i,j] V_j) / l_i
     lse_i  = m_i + ln(l_i)                      (natural log of sum_j exp(S[i,j]))
 
+Sliding window (the pages name sliding-window attention among the custom
+attention variants a tiled kernel is suited to, "Triton: CUDA-level operators
+in Python", section "when to use Triton", without defining it; the reading
+taken here is the usual local band).  With window W >= 1 a key j is kept for
+query i only if, in addition to the causal rule,
+
+    i - W < j                (the W most recent keys, the diagonal included)
+    j < i + W                (non-causal only: the symmetric band |i - j| < W)
+
+and W = 0 means no window.  Every row keeps at least key i.
+
 All arithmetic is float64 on the exact input values (fp16/bf16 upcast).  The
 scale is taken as float64(float32(scale)), i.e. exactly the float32 value the
 library receives.  The logsumexp output is not on the pages; it is the natural
@@ -44,15 +55,20 @@ def _scale64(scale: float) -> np.float64:
     return np.float64(np.float32(scale))
 
 
-def _head(qh, kh, vh, causal: bool, scale64, rows):
+def _head(qh, kh, vh, causal: bool, scale64, rows, window: int = 0):
     """One (b, h): qh [N, d], kh [N, d], vh [N, d]; rows = query indices to produce.
 
     Returns O [R, d], lse [R], W [R, N] (the normalised softmax weights)."""
     s = scale64 * (qh[rows] @ kh.T)                       # [R, N]
+    j = np.arange(kh.shape[0])[None, :]
+    i = rows[:, None]
     if causal:
-        j = np.arange(kh.shape[0])[None, :]
-        s = np.where(j > rows[:, None], -np.inf, s)
-    m = s.max(axis=1)                                     # every row keeps key 0, so m is finite
+        s = np.where(j > i, -np.inf, s)
+    if window > 0:
+        s = np.where(j <= i - window, -np.inf, s)
+        if not causal:
+            s = np.where(j >= i + window, -np.inf, s)
+    m = s.max(axis=1)                                     # every row keeps key i, so m is finite
     p = np.exp(s - m[:, None])
     l = p.sum(axis=1)
     o = (p @ vh) / l[:, None]
@@ -67,7 +83,7 @@ def _rows_for(rows, b, h, n):
     return rows if rows.ndim == 1 else rows[b, h]
 
 
-def attention(q, k, v, causal, scale, rows=None):
+def attention(q, k, v, causal, scale, rows=None, window=0):
     """Exact attention forward.
 
     q, k, v : [B, H, N, d] (torch CPU tensors or arrays, any float dtype)
@@ -75,8 +91,13 @@ def attention(q, k, v, causal, scale, rows=None):
     scale   : the score scale (used as float64(float32(scale)))
     rows    : None for every query row, an int array [R] of rows used for every
               head, or [B, H, R] per head
+    window  : 0 for none, else W >= 1: key j also needs i - W < j (and j < i + W
+              when not causal)
     returns : O [B, H, R, d] float64, lse [B, H, R] float64 (natural log)
     """
+    window = int(window)
+    if window < 0:
+        raise ValueError("window must be >= 0")
     q, k, v = _f64(q), _f64(k), _f64(v)
     B, H, N, d = q.shape
     s64 = _scale64(scale)
@@ -86,11 +107,11 @@ def attention(q, k, v, causal, scale, rows=None):
     for b in range(B):
         for h in range(H):
             r = _rows_for(rows, b, h, N)
-            O[b, h], L[b, h], _ = _head(q[b, h], k[b, h], v[b, h], bool(causal), s64, r)
+            O[b, h], L[b, h], _ = _head(q[b, h], k[b, h], v[b, h], bool(causal), s64, r, window)
     return O, L
 
 
-def softmax_weights(q, k, causal, scale):
+def softmax_weights(q, k, causal, scale, window=0):
     """The normalised weights P/l [B, H, N, N] of the definition (small shapes only)."""
     q, k = _f64(q), _f64(k)
     B, H, N, d = q.shape
@@ -99,5 +120,5 @@ def softmax_weights(q, k, causal, scale):
     zeros = np.zeros((N, 1))
     for b in range(B):
         for h in range(H):
-            _, _, W[b, h] = _head(q[b, h], k[b, h], zeros, bool(causal), s64, np.arange(N))
+            _, _, W[b, h] = _head(q[b, h], k[b, h], zeros, bool(causal), s64, np.arange(N), int(window))
     return W
