@@ -7,7 +7,10 @@ roofline of the kernel against the dense bf16/fp16 MFMA peak and the CPU
 oracle's throughput on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--causal 0|1]
-                    [--no-cpu-baseline] [--cpu-seconds S]
+                    [--window W] [--no-cpu-baseline] [--cpu-seconds S]
+
+--window W times attn_fwd_window (sliding window, key j kept for query i only if
+i - W < j, and j < i + W when not causal) and credits 4*d FLOPs per kept pair.
 
 Traffic calibration (run each under rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE):
     python bench.py --copy-calibration          # plain 256 MiB copy kernel, known bytes
@@ -28,17 +31,29 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak, causal N=4096 d=128"
+METRIC_WINDOW = "sliding-window attention fwd TFLOP/s (4*d per kept query-key pair) and % of bf16 MFMA peak"
 MFMA_PEAK_TFLOPS = 2516.6      # dense fp16/bf16: 256 CU x 4096 FLOP/clk x 2.4 GHz (the 2.5 PFLOP/s figure)
 KERNEL_SOURCE = os.path.join(ROOT, "exact_tiled_attention_03_amd", "csrc", "attn_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source's code: comments and whitespace are dropped, so that
+    editing a comment does not invalidate counters taken on the same code."""
+    import re
+    with open(KERNEL_SOURCE) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
-def measured_traffic(workload: str, causal: int):
+def traffic_key(workload: str, causal: int, window: int = 0) -> str:
+    return f"{workload}-causal{causal}" + (f"-window{window}" if window > 0 else "")
+
+
+def measured_traffic(workload: str, causal: int, window: int = 0):
     """HBM bytes per launch from the committed rocprofv3 counter runs, or None when
     absent or when the kernel source changed since they were taken."""
     try:
@@ -46,7 +61,7 @@ def measured_traffic(workload: str, causal: int):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = t.get(f"{workload}-causal{causal}")
+    entry = t.get(traffic_key(workload, causal, window))
     if not entry or entry.get("source_sha256_16") != source_hash():
         return None
     return entry.get("bytes_per_launch")
@@ -79,7 +94,7 @@ def _pmc_kib_per_dispatch(directory: str, counter: str, kernel_substr: str) -> f
     return statistics.median(vals.values())
 
 
-def traffic_summary(attn_fetch, attn_write, copy_fetch, copy_write, workload, causal):
+def traffic_summary(attn_fetch, attn_write, copy_fetch, copy_write, workload, causal, window=0):
     """HBM bytes per attention launch: FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by
     the ratio of known bytes to what the same counter reads for the plain copy kernel."""
     f_copy = _pmc_kib_per_dispatch(copy_fetch, "FETCH_SIZE", "elementwise") * 1024
@@ -97,13 +112,36 @@ def traffic_summary(attn_fetch, attn_write, copy_fetch, copy_write, workload, ca
             table = json.load(f)
     except (OSError, ValueError):
         table = {}
-    table[f"{workload}-causal{causal}"] = entry
+    key = traffic_key(workload, causal, window)
+    table[key] = entry
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(table, f, indent=1, sort_keys=True)
-    print(json.dumps({f"{workload}-causal{causal}": entry}))
+    print(json.dumps({key: entry}))
 
 
-def cpu_baseline(w, causal, q, k, v, out, lse, budget_s: float):
+def kept_pairs(n: int, causal: int, window: int, rows=None) -> float:
+    """Number of (query, key) pairs the mask keeps in one head (for the given query
+    rows, default all): key j is kept for query i when j <= i (causal) and, with a
+    window W >= 1, i - W < j (and j < i + W when not causal)."""
+    import numpy as np
+    i = np.arange(n, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    lo = np.maximum(0, i - window + 1) if window > 0 else np.zeros_like(i)
+    if causal:
+        hi = i
+    else:
+        hi = np.minimum(n - 1, i + window - 1) if window > 0 else np.full_like(i, n - 1)
+    return float((hi - lo + 1).sum())
+
+
+def launch_flops(w, causal: int, window: int) -> float:
+    """FLOPs credited to one launch: 4*B*H*N^2*d, halved when causal (the metric's
+    convention); with a window, 4*d per kept (query, key) pair."""
+    if window <= 0:
+        return w.flops(causal)
+    return 4.0 * w.d * w.B * w.H * kept_pairs(w.N, causal, window)
+
+
+def cpu_baseline(w, causal, q, k, v, out, lse, budget_s: float, window: int = 0):
     """Time the float64 oracle on whole heads of the same workload until ~budget_s
     of CPU work; also re-check the GPU output of those heads against it."""
     import numpy as np
@@ -115,7 +153,7 @@ def cpu_baseline(w, causal, q, k, v, out, lse, budget_s: float):
         blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
         qc, kc, vc = q.cpu(), k.cpu(), v.cpu()
         oc, lc = out.cpu().double().numpy(), lse.cpu().double().numpy()
-        flops_per_head = w.flops(causal) / (w.B * w.H)
+        flops_per_head = launch_flops(w, causal, window) / (w.B * w.H)
         heads, t0, max_err, lse_err = 0, time.perf_counter(), 0.0, 0.0
         rows = None
         if w.N > 8192:   # long sequences: the oracle's rows are sampled per head
@@ -123,7 +161,7 @@ def cpu_baseline(w, causal, q, k, v, out, lse, budget_s: float):
         for idx in range(w.B * w.H):
             b, h = divmod(idx, w.H)
             O, L = oracle.attention(qc[b:b + 1, h:h + 1], kc[b:b + 1, h:h + 1], vc[b:b + 1, h:h + 1],
-                                    causal, w.scale, rows=rows)
+                                    causal, w.scale, rows=rows, window=window)
             sel = slice(None) if rows is None else rows
             max_err = max(max_err, float(np.abs(oc[b, h][sel] - O[0, 0]).max()))
             lse_err = max(lse_err, float(np.abs(lc[b, h][sel] - L[0, 0]).max()))
@@ -135,8 +173,8 @@ def cpu_baseline(w, causal, q, k, v, out, lse, budget_s: float):
         flops = heads * flops_per_head
         sample = f"{heads} of {w.B * w.H} heads, all {w.N} rows each"
     else:
-        # causal rows cost in proportion to their key count
-        keys = (rows + 1).sum() if causal else len(rows) * w.N
+        # rows cost in proportion to their kept key count
+        keys = kept_pairs(w.N, causal, window, rows) if window > 0 else ((rows + 1).sum() if causal else len(rows) * w.N)
         flops = heads * 4.0 * keys * w.d
         sample = f"{heads} of {w.B * w.H} heads, {len(rows)} seeded rows each"
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
@@ -151,6 +189,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline workload)")
     ap.add_argument("--causal", type=int, default=None)
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window W >= 1 (attn_fwd_window); FLOPs then count kept pairs x 4d")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -160,7 +200,8 @@ def main():
     if args.traffic_summary:
         import attn_workloads as aw
         w = aw.by_name(args.workload) if args.workload else aw.WORKLOADS[aw.HEADLINE]
-        traffic_summary(*args.traffic_summary, w.name, w.causal_modes[0] if args.causal is None else args.causal)
+        traffic_summary(*args.traffic_summary, w.name, w.causal_modes[0] if args.causal is None else args.causal,
+                        args.window)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -186,7 +227,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     for _ in range(args.warmup):
-        eta.attn_fwd(q, k, v, out, lse, causal, w.scale, stream=stream)
+        eta.attn_fwd(q, k, v, out, lse, causal, w.scale, stream=stream, window=args.window)
     torch.cuda.synchronize()
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -197,7 +238,7 @@ def main():
     t_begin.record(stream)
     for i in range(args.steps):
         starts[i].record(stream)
-        eta.attn_fwd(q, k, v, out, lse, causal, w.scale, stream=stream)
+        eta.attn_fwd(q, k, v, out, lse, causal, w.scale, stream=stream, window=args.window)
         ends[i].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
@@ -206,12 +247,12 @@ def main():
     per_launch = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     ms_per_step = total_ms / args.steps
     launch_ms = statistics.mean(per_launch)
-    flops = w.flops(causal)
+    flops = launch_flops(w, causal, args.window)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (launch_ms * 1e-3) / 1e12
 
     line = {
-        "metric": METRIC,
+        "metric": METRIC if args.window <= 0 else METRIC_WINDOW,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -223,19 +264,21 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded iid N(0,1) Q, K, V)",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": causal,
+        "config": {"workload": w.name + (f"-window{args.window}" if args.window > 0 else ""),
+                   "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": causal, "window": args.window,
                    "scale": w.scale, "layout": "[B,H,N,d] contiguous", "pct_of_mfma_peak": round(100 * value / MFMA_PEAK_TFLOPS, 2),
                    "launch_ms_median": round(statistics.median(per_launch), 5),
                    "launch_ms_p95": round(sorted(per_launch)[int(0.95 * (len(per_launch) - 1))], 5),
                    "launch_ms_min": round(min(per_launch), 5)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_PEAK_TFLOPS, 4), "traffic": measured_traffic(w.name, causal),
+                     "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(w.name, causal, args.window),
                      "kernel": f"attn_fwd_kernel<{w.d},{'bf16' if w.dtype == 'bf16' else 'f16'},{'causal' if causal else 'full'}>",
                      "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": w.algorithmic_bytes()},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, causal, q, k, v, out, lse, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(w, causal, q, k, v, out, lse, args.cpu_seconds, args.window)
     print(json.dumps(line), flush=True)
 
 

@@ -40,6 +40,10 @@ def load_library():
                              ctypes.c_int, ctypes.c_void_p]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [ctypes.c_int]
+    lib.attn_fwd_window.restype = ctypes.c_int
+    lib.attn_fwd_window.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
     lib.attn_fwd_schedule.restype = ctypes.c_int
     lib.attn_fwd_schedule.argtypes = [ctypes.c_int] * 5
     _lib = lib
@@ -75,11 +79,13 @@ def _stream_handle(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def attn_fwd(q, k, v, out, lse, causal: bool, scale: float, stream=None) -> None:
+def attn_fwd(q, k, v, out, lse, causal: bool, scale: float, stream=None, window: int = 0) -> None:
     """Enqueue the forward pass on `stream` (default: torch's current stream).
 
     q, k, v, out: contiguous [B, H, N, d] float16/bfloat16 tensors on the GPU.
     lse: contiguous [B, H, N] float32 tensor on the GPU, or None.
+    window: 0 for full attention (attn_fwd), W >= 1 for the sliding window of
+    attn_fwd_window (key j kept only if i - W < j, and j < i + W when not causal).
     Raises AttnError with the library's status on rejected arguments."""
     lib = load_library()
     if q.dim() != 4:
@@ -100,19 +106,25 @@ def attn_fwd(q, k, v, out, lse, causal: bool, scale: float, stream=None) -> None
         import torch
         if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N):
             raise ValueError("lse must be float32 [B, H, N]")
-    st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                      lse.data_ptr() if lse is not None else None,
-                      B, H, N, d, int(bool(causal)), float(scale), _dtype_code(q), _stream_handle(stream))
+    lse_ptr = lse.data_ptr() if lse is not None else None
+    if window:
+        st = lib.attn_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
+                                 B, H, N, d, int(bool(causal)), int(window), float(scale), _dtype_code(q),
+                                 _stream_handle(stream))
+    else:
+        st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
+                          B, H, N, d, int(bool(causal)), float(scale), _dtype_code(q), _stream_handle(stream))
     if st != ATTN_OK:
         raise AttnError(st, attn_status_string(st))
 
 
-def attention(q, k, v, causal: bool, scale: float, stream=None):
-    """Allocate out [B,H,N,d] and lse [B,H,N] with torch, then call attn_fwd."""
+def attention(q, k, v, causal: bool, scale: float, stream=None, window: int = 0):
+    """Allocate out [B,H,N,d] and lse [B,H,N] with torch, then call attn_fwd (or
+    attn_fwd_window when window > 0)."""
     import torch
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
-    attn_fwd(q, k, v, out, lse, causal, scale, stream)
+    attn_fwd(q, k, v, out, lse, causal, scale, stream, window)
     return out, lse
 
 

@@ -6,7 +6,11 @@
 // m and running sum l of the exponentials; the fp32 output accumulator is
 // rescaled by exp(m_old - m_new) when the max grows and divided by l once after
 // the loop.  Keys with index > query index are excluded when causal.  The
-// N x N score matrix never leaves registers.
+// N x N score matrix never leaves registers.  The sliding-window variant (a
+// variant "Triton: CUDA-level operators in Python" names without defining; read
+// as the local band i - W < j, and j < i + W when not causal) only narrows the
+// range of key tiles a query tile visits and adds a lower mask limit on the
+// tiles that straddle the band's edge; it is a compile-time kernel parameter.
 //
 // gfx950 mapping (not taken from the pages, which target NVIDIA tensor cores):
 //
@@ -105,6 +109,7 @@ struct FwdArgs {
     int ngroups;       // work-groups per head: causal pairs tiles (i, nqt-1-i), else nqt
     float c;           // |scale| * log2(e), > 0
     unsigned qsign;    // 0x80008000 when scale < 0 (Q negated exactly), else 0
+    int window;        // 0: none; W in [1, N): key j kept for query i only if i - W < j (and j < i + W if not causal)
 };
 
 // x combined with the value in the lane 32 positions away (the other half of
@@ -201,13 +206,13 @@ __device__ __forceinline__ void map_workgroup(const FwdArgs& a, int& bh, int& gr
 
 // State and arithmetic of one wave: 32 query rows (one per accumulator column;
 // the two lanes of a column each hold half of the keys of a tile).
-template <int D, int DT, bool CAUSAL, int WAVES>
+template <int D, int DT, bool CAUSAL, int WAVES, bool WIN>
 struct Wave {
     using C = Cfg<D, WAVES>;
     using E = Elem<DT>;
     static constexpr int SB = C::SB, KK = C::KK, KSTEPS = C::KSTEPS, DBLK = C::DBLK, CPR = C::CPR;
 
-    int lane, wave, hf, n, N, qw0, qi;
+    int lane, wave, hf, n, N, qw0, qi, W;
     float c;
     unsigned lds0;
     const unsigned char* kbase;
@@ -225,6 +230,7 @@ struct Wave {
         hf = lane >> 5;
         n = lane & 31;
         N = a.N;
+        W = WIN ? a.window : 0;          // a compile-time 0 without a window: its tests fold away
         c = a.c;
         lds0 = lds_base;
         // direct-load slot (it, wave, lane) of a tile holds row r = slot / CPRP,
@@ -296,7 +302,15 @@ struct Wave {
     __device__ __forceinline__ int slot_base(int it) const { return (it * C::WAVES + wave) * 64; }
 
     // does this wave have keys to process in tile j?
-    __device__ __forceinline__ bool active(int j) const { return qw0 < N && (!CAUSAL || j * C::BN <= qw0 + 31); }
+    // (the rows qw0 .. qw0+31 keep keys up to qw0+31 when causal, and within the
+    // window band [qi-W+1, qi+W-1] otherwise)
+    __device__ __forceinline__ bool active(int j) const {
+        if (qw0 >= N) return false;
+        const int klo = j * C::BN, khi = klo + C::BN - 1;
+        if (CAUSAL && klo > qw0 + 31) return false;
+        if (W > 0 && (khi < qw0 - W + 1 || (!CAUSAL && klo > qw0 + 31 + W - 1))) return false;
+        return true;
+    }
 
     // S^T = K Q^T for the tile in K stage ST: two independent 32-key accumulators
     template <int ST>
@@ -316,15 +330,21 @@ struct Wave {
     // the same m, so the result is unchanged.
     __device__ __forceinline__ void prepare(f32x16_t (&s)[SB], int j) {
         const int kt0 = j * C::BN;
-        if ((CAUSAL && kt0 + C::BN - 1 > qw0) || kt0 + C::BN > N) {
+        const bool window_edge = W > 0 && (kt0 < qw0 + 32 - W || (!CAUSAL && kt0 + C::BN - 1 > qw0 + W - 1));
+        if ((CAUSAL && kt0 + C::BN - 1 > qw0) || kt0 + C::BN > N || window_edge) {
             // key index of register i is kt0 + 8*hf + 32*sb + 16*(i/8) + i%8; it is
-            // kept iff that is <= lim (the query for causal, N-1 for the tail)
-            const int lim = (CAUSAL ? min(qi, N - 1) : N - 1) - (kt0 + 8 * hf);
+            // kept iff lo <= that <= hi: hi is the query for causal (else the band's
+            // upper end, else N-1), capped at N-1; lo is the band's lower end
+            const int base = kt0 + 8 * hf;
+            const int hi = (CAUSAL ? min(qi, N - 1) : (W > 0 ? min(qi + W - 1, N - 1) : N - 1)) - base;
+            const int lo = (W > 0 ? qi - W + 1 : 0) - base;
 #pragma unroll
             for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    if (32 * sb + 16 * (i >> 3) + (i & 7) > lim) s[sb][i] = kNegInf;
+                for (int i = 0; i < 16; ++i) {
+                    const int key = 32 * sb + 16 * (i >> 3) + (i & 7);
+                    if (key > hi || (WIN && key < lo)) s[sb][i] = kNegInf;
+                }
         }
         float mx = kNegInf;
 #pragma unroll
@@ -400,7 +420,7 @@ struct Wave {
 #endif  // __HIP_DEVICE_COMPILE__
 
 // ---- the kernel: WAVES free-running waves per work-group ---------------------
-template <int D, int DT, bool CAUSAL, int WAVES>
+template <int D, int DT, bool CAUSAL, int WAVES, bool WIN>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
@@ -408,7 +428,7 @@ void attn_fwd_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    Wave<D, DT, CAUSAL, WAVES> w;
+    Wave<D, DT, CAUSAL, WAVES, WIN> w;
     w.init(a, (unsigned)(size_t)(lds_bytes)smem, tid, wave);
 
     int bh, grp;
@@ -418,8 +438,12 @@ void attn_fwd_kernel(FwdArgs a) {
         const int qt = CAUSAL ? (item == 0 ? a.nqt - 1 - grp : grp) : grp;
         const int q0 = qt * C::BM;
         w.begin(a, bh, q0 + 32 * wave);
-        const int kend = CAUSAL ? min(a.N, q0 + C::BM) : a.N;
+        // key tiles jlo .. nt-1: up to the last query (causal) or its band's end,
+        // from the first query's band start
+        const int win = WIN ? a.window : 0;
+        const int kend = CAUSAL ? min(a.N, q0 + C::BM) : (win > 0 ? min(a.N, q0 + C::BM - 1 + win) : a.N);
         const int nt = (kend + C::BN - 1) / C::BN;
+        const int jlo = win > 0 ? max(0, q0 - win + 1) / C::BN : 0;
 
         // one step: prefetch tile j+1 into the other stage, compute tile j, sync.
         // The wave raises its priority while it issues the score MFMAs, so the
@@ -444,11 +468,11 @@ void attn_fwd_kernel(FwdArgs a) {
             wait_loads();
             __syncthreads();
         };
-        w.issue(false, 0, 0);
-        w.issue(true, 0, 0);
+        w.issue(false, jlo, 0);
+        w.issue(true, jlo, 0);
         wait_loads();
         __syncthreads();
-        for (int j = 0; j < nt; j += 2) {
+        for (int j = jlo; j < nt; j += 2) {                 // tile j in stage (j - jlo) & 1
             step(std::integral_constant<int, 0>{}, j);
             if (j + 1 < nt) step(std::integral_constant<int, 1>{}, j + 1);
         }
@@ -472,20 +496,23 @@ bool use_wide(long long bh, long long N, int causal) {
     return (causal ? (nqt + 1) / 2 : nqt) * bh >= kWideMinGroups;
 }
 
-template <int D, int DT, bool CAUSAL, int WAVES>
+template <int D, int DT, bool CAUSAL, int WAVES, bool WIN>
 hipError_t launch_waves(FwdArgs a, hipStream_t stream) {
     constexpr int BM = Cfg<D, WAVES>::BM;
     const long long nqt = ((long long)a.N + BM - 1) / BM;
     a.nqt = (int)nqt;
     a.ngroups = CAUSAL ? (int)((nqt + 1) / 2) : (int)nqt;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, CAUSAL, WAVES>), dim3((unsigned)a.ngroups * (unsigned)a.BH),
+    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, CAUSAL, WAVES, WIN>), dim3((unsigned)a.ngroups * (unsigned)a.BH),
                        dim3(64 * WAVES), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int D, int DT, bool CAUSAL>
 hipError_t launch(FwdArgs a, hipStream_t stream) {
-    return use_wide(a.BH, a.N, CAUSAL) ? launch_waves<D, DT, CAUSAL, 8>(a, stream) : launch_waves<D, DT, CAUSAL, 4>(a, stream);
+    const bool wide = use_wide(a.BH, a.N, CAUSAL);
+    if (a.window > 0)
+        return wide ? launch_waves<D, DT, CAUSAL, 8, true>(a, stream) : launch_waves<D, DT, CAUSAL, 4, true>(a, stream);
+    return wide ? launch_waves<D, DT, CAUSAL, 8, false>(a, stream) : launch_waves<D, DT, CAUSAL, 4, false>(a, stream);
 }
 
 template <int D, int DT>
@@ -535,13 +562,16 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 }  // namespace
 
-extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
-                        int B, int H, int N, int d, int causal, float scale, int dtype, void* stream) {
+namespace {
+
+int fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int N, int d, int causal,
+        int window, float scale, int dtype, void* stream) {
     if (!q || !k || !v || !out) return ATTN_ERR_NULL;
     if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
     if (d != 64 && d != 80 && d != 128) return ATTN_ERR_HEAD_DIM;
     if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
     if (causal != 0 && causal != 1) return ATTN_ERR_CAUSAL;
+    if (window < 0) return ATTN_ERR_WINDOW;
     if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15u) return ATTN_ERR_ALIGN;
     if ((uintptr_t)lse & 3u) return ATTN_ERR_ALIGN;
@@ -575,6 +605,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
     // smallest normal float, which makes every exponent round to exactly 0
     a.c = scale == 0.f ? FLT_MIN : std::fabs(scale) * kLog2e;
     a.qsign = std::signbit(scale) && scale != 0.f ? 0x80008000u : 0u;
+    a.window = window >= N ? 0 : window;   // a band of N or more keeps every key the mask allows
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
@@ -584,6 +615,19 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
         default: err = dispatch_dtype<128>(a, dtype, causal, s); break;
     }
     return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
+                        int B, int H, int N, int d, int causal, float scale, int dtype, void* stream) {
+    return fwd(q, k, v, out, lse, B, H, N, d, causal, 0, scale, dtype, stream);
+}
+
+extern "C" int attn_fwd_window(const void* q, const void* k, const void* v, void* out, float* lse,
+                               int B, int H, int N, int d, int causal, int window, float scale, int dtype,
+                               void* stream) {
+    return fwd(q, k, v, out, lse, B, H, N, d, causal, window, scale, dtype, stream);
 }
 
 extern "C" int attn_fwd_schedule(int B, int H, int N, int d, int causal) {
@@ -605,6 +649,7 @@ extern "C" const char* attn_status_string(int status) {
         case ATTN_ERR_LAUNCH: return "kernel launch failed";
         case ATTN_ERR_CAUSAL: return "causal must be 0 or 1";
         case ATTN_ERR_ALIAS: return "out or lse overlaps an input or each other";
+        case ATTN_ERR_WINDOW: return "window must be >= 0";
         default: return "unknown status";
     }
 }

@@ -45,7 +45,8 @@ typedef enum {
     ATTN_ERR_DEVICE = 7,    /* no current HIP device, or it is not a gfx950 */
     ATTN_ERR_LAUNCH = 8,    /* the kernel launch returned an error */
     ATTN_ERR_CAUSAL = 9,    /* causal is neither 0 nor 1 */
-    ATTN_ERR_ALIAS = 10     /* out or lse overlaps q, k, v, or each other */
+    ATTN_ERR_ALIAS = 10,    /* out or lse overlaps q, k, v, or each other */
+    ATTN_ERR_WINDOW = 11    /* window is negative */
 } attn_status;
 
 /*
@@ -87,7 +88,31 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
              void* stream);
 
 /*
- * attn_fwd_schedule -- which kernel schedule attn_fwd uses for a shape.
+ * attn_fwd_window -- attn_fwd restricted to a sliding window (local band).
+ *
+ * "Triton: CUDA-level operators in Python" (f.mffb.com.cn), section "when to
+ * use Triton", names sliding-window attention as one of the attention variants
+ * a tiled kernel serves, without defining it; the reading implemented is the
+ * usual local band.  With window = W >= 1, key j is kept for query i only if
+ *
+ *     i - W < j                  (the W most recent keys, the diagonal included)
+ *     j < i + W                  (causal = 0 only: the symmetric band |i - j| < W)
+ *
+ * on top of the causal rule when causal = 1.  window = 0 (or W >= N, which keeps
+ * every key) gives exactly attn_fwd.  lse is over the kept keys.  Tiles wholly
+ * outside every row's band are never loaded or computed: the work is
+ * proportional to N * min(N, W) instead of N^2.
+ *
+ * Arguments, layout, ownership, arithmetic and errors as attn_fwd; in addition
+ * ATTN_ERR_WINDOW when window < 0.
+ */
+int attn_fwd_window(const void* q, const void* k, const void* v, void* out, float* lse,
+                    int B, int H, int N, int d, int causal, int window, float scale, int dtype,
+                    void* stream);
+
+/*
+ * attn_fwd_schedule -- which kernel schedule attn_fwd (and attn_fwd_window,
+ * which makes the same choice) uses for a shape.
  *
  * Returns ATTN_SCHEDULE_SMALL (4 waves, 128 queries per work-group, two
  * work-groups per CU) or ATTN_SCHEDULE_WIDE (8 waves, 256 queries per

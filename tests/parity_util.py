@@ -14,13 +14,14 @@ MEAN_ABS = 1e-3
 LSE_ABS = 1e-3
 
 
-def run_gpu(q, k, v, causal, scale, with_lse=True, stream=None):
-    """q, k, v: CPU tensors.  Returns (out, lse) as CPU tensors (lse None if skipped)."""
+def run_gpu(q, k, v, causal, scale, with_lse=True, stream=None, window=0):
+    """q, k, v: CPU tensors.  Returns (out, lse) as CPU tensors (lse None if skipped).
+    window > 0 goes through attn_fwd_window."""
     import exact_tiled_attention_03_amd as eta
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     out = torch.empty_like(qd)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda") if with_lse else None
-    eta.attn_fwd(qd, kd, vd, out, lse, causal, scale, stream=stream)
+    eta.attn_fwd(qd, kd, vd, out, lse, causal, scale, stream=stream, window=window)
     torch.cuda.synchronize()
     return out.cpu(), (lse.cpu() if with_lse else None)
 
@@ -36,9 +37,9 @@ def gather_rows(x: np.ndarray, rows):
     return np.stack([np.stack([x[b, h, rows[b, h]] for h in range(H)]) for b in range(B)])
 
 
-def errors(out, lse, q, k, v, causal, scale, rows=None):
+def errors(out, lse, q, k, v, causal, scale, rows=None, window=0):
     """Max-abs / mean-abs error of out and max-abs error of lse against the oracle."""
-    O, L = oracle.attention(q, k, v, causal, scale, rows=rows)
+    O, L = oracle.attention(q, k, v, causal, scale, rows=rows, window=window)
     og = gather_rows(out.double().numpy(), rows)
     e = np.abs(og - O)
     res = {"max_abs": float(e.max()), "mean_abs": float(e.mean())}
@@ -60,7 +61,7 @@ def unit_roundoff(dtype) -> float:
     return 2.0 ** -8 if dtype in ("bf16", torch.bfloat16) else 2.0 ** -11
 
 
-def assert_within_derived_bound(out, lse, q, k, v, causal, scale, rows=None, label=""):
+def assert_within_derived_bound(out, lse, q, k, v, causal, scale, rows=None, label="", window=0):
     """Bar for shapes beyond the five workloads.
 
     The method rounds the probabilities to the input type before P V and the
@@ -74,8 +75,8 @@ def assert_within_derived_bound(out, lse, q, k, v, causal, scale, rows=None, lab
     be within max(1e-3, the mean of the same bound), since with very few keys the
     output rounding alone averages about 1e-3 in bf16; lse keeps the plain bar."""
     u = unit_roundoff(q.dtype)
-    O, L = oracle.attention(q, k, v, causal, scale, rows=rows)
-    A, _ = oracle.attention(q, k, v.abs(), causal, scale, rows=rows)
+    O, L = oracle.attention(q, k, v, causal, scale, rows=rows, window=window)
+    A, _ = oracle.attention(q, k, v.abs(), causal, scale, rows=rows, window=window)
     og = gather_rows(out.double().numpy(), rows)
     e = np.abs(og - O)
     derived = u * A + u * (np.abs(O) + u * A) + 1e-5 * (1.0 + A)

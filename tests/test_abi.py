@@ -34,7 +34,7 @@ def declared_enum(name_prefix):
 
 
 def test_header_declares_entry_points():
-    assert declared_functions() == ["attn_fwd", "attn_fwd_schedule", "attn_status_string"]
+    assert declared_functions() == ["attn_fwd", "attn_fwd_schedule", "attn_fwd_window", "attn_status_string"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -80,6 +80,30 @@ def call(lib, q=A, k=A + SZ, v=A + 2 * SZ, out=A + 3 * SZ, lse=A + 4 * SZ, B=1, 
 ])
 def test_argument_validation(lib, kw, code):
     assert call(lib, **kw) == code, eta.attn_status_string(code)
+
+
+def call_window(lib, window, **kw):
+    a = dict(q=A, k=A + SZ, v=A + 2 * SZ, out=A + 3 * SZ, lse=A + 4 * SZ, B=1, H=1, N=16, d=64, causal=1,
+             scale=0.125, dtype=0)
+    a.update(kw)
+    return lib.attn_fwd_window(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                               a["causal"], window, a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("window,kw,code", [
+    (-1, {}, 11), (-100, dict(causal=0), 11),
+    (4, dict(q=None), 1), (4, dict(d=96), 3), (4, dict(causal=2), 9), (4, dict(scale=math.nan), 5),
+    (4, dict(out=A + 64), 10), (4, dict(B=0), 2),
+])
+def test_window_argument_validation(lib, window, kw, code):
+    assert call_window(lib, window, **kw) == code, eta.attn_status_string(code)
+
+
+def test_window_valid_arguments_reach_the_device_check(lib):
+    if gpu_available():
+        pytest.skip("device check refuses only where no gfx950 is current")
+    for w in (0, 1, 7, 16, 10**9):
+        assert call_window(lib, w) == 7
 
 
 def test_lse_may_be_null_then_device_is_checked(lib):

@@ -1,0 +1,29 @@
+"""Host-side logic of bench.py (no GPU): the FLOPs credited per launch."""
+import bench
+import attn_workloads as aw
+
+
+def brute_pairs(n, causal, window):
+    return sum(1 for i in range(n) for j in range(n)
+               if (not causal or j <= i) and (window == 0 or (i - window < j and (causal or j < i + window))))
+
+
+def test_kept_pairs_matches_enumeration():
+    for n in (1, 2, 7, 33):
+        for causal in (0, 1):
+            for window in (0, 1, 2, 5, 32, 33, 100):
+                assert bench.kept_pairs(n, causal, window) == brute_pairs(n, causal, window)
+
+
+def test_kept_pairs_on_rows_subset():
+    rows = [0, 3, 9]
+    assert bench.kept_pairs(10, 1, 4, rows) == 1 + 4 + 4
+    assert bench.kept_pairs(10, 0, 4, rows) == 4 + 7 + 4
+
+
+def test_launch_flops_conventions():
+    w = aw.WORKLOADS[aw.HEADLINE]
+    assert bench.launch_flops(w, 1, 0) == w.flops(1) == 2.0 * w.B * w.H * w.N ** 2 * w.d
+    # a window of N keeps every causal pair: N(N+1)/2 per head, not the N^2/2 convention
+    assert bench.launch_flops(w, 1, w.N) == 4.0 * w.d * w.B * w.H * w.N * (w.N + 1) / 2
+    assert bench.launch_flops(w, 0, 1) == 4.0 * w.d * w.B * w.H * w.N
