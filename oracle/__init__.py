@@ -4,5 +4,6 @@ TEST INFRASTRUCTURE ONLY: used by tests/, the smoke check and the benchmark's
 CPU-baseline leg.  The HIP library never imports it.
 """
 from .attention import attention, softmax_weights
+from .softmax import softmax_rows
 
-__all__ = ["attention", "softmax_weights"]
+__all__ = ["attention", "softmax_weights", "softmax_rows"]
