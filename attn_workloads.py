@@ -1,9 +1,9 @@
-"""Seeded synthetic workloads for the attention forward pass.
+"""Seeded synthetic workloads for the attention forward pass and the row softmax.
 
 This module is shared by the tests, the benchmark and smoke check.  It draws
 inputs and sample rows and holds the table of workload shapes; it contains none
-of the attention arithmetic, so neither the CPU oracle nor the HIP library
-depends on the other through it.
+of the attention or softmax arithmetic, so neither the CPU oracle nor the HIP
+library depends on the other through it.
 
 Recipe (identical for every consumer):
   * numpy ``default_rng(seed)``, seed = 1000 + workload index;
@@ -25,7 +25,7 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16}
+DTYPES = {"fp16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
 
 
 @dataclass(frozen=True)
@@ -119,3 +119,59 @@ def sample_rows(B: int, H: int, N: int, count: int, seed: int) -> np.ndarray:
             rest = rng.choice(rest_pool, size=count - forced.size, replace=False)
             out[b, h] = np.sort(np.concatenate([forced, rest]))
     return out
+
+
+# --- row softmax ---------------------------------------------------------------
+#
+# Recipe: numpy default_rng(seed); x drawn as iid N(0, sigma^2) float32 of shape
+# [rows, cols] (sigma = 1 is the distribution of the scaled attention scores of
+# unit-normal q and k); then cast to the workload's type by torch on the CPU
+# (round to nearest even).  The shape of the benchmark workload is the one the
+# pages quote the fused softmax's bandwidth at: rows of 32K columns ("Triton:
+# CUDA-level operators in Python", example 2).
+
+
+@dataclass(frozen=True)
+class SoftmaxWorkload:
+    name: str
+    rows: int
+    cols: int
+    dtype: str          # "f32" | "fp16" | "bf16"
+    seed: int
+    sigma: float = 1.0
+    note: str = field(default="", compare=False)
+
+    def algorithmic_bytes(self) -> int:
+        """x read once and y written once (the fused kernel's HBM traffic)."""
+        es = 4 if self.dtype == "f32" else 2
+        return 2 * self.rows * self.cols * es
+
+
+SOFTMAX_WORKLOADS = [
+    SoftmaxWorkload("softmax_rows4096_cols32768_f32", 4096, 32768, "f32", 2000,
+                    note="rows of 32K columns, fp32"),
+    SoftmaxWorkload("softmax_rows4096_cols32768_bf16", 4096, 32768, "bf16", 2001),
+    SoftmaxWorkload("softmax_rows1024_cols262147_f32", 1024, 262147, "f32", 2002,
+                    note="rows beyond the in-register limit, ragged"),
+]
+
+
+def softmax_by_name(name: str) -> SoftmaxWorkload:
+    for w in SOFTMAX_WORKLOADS:
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
+def draw_rows(rows: int, cols: int, seed: int, sigma: float = 1.0) -> np.ndarray:
+    """x as a float32 numpy array [rows, cols] following the recipe above."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, cols), dtype=np.float32)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    return x
+
+
+def make_rows(rows: int, cols: int, dtype: str, seed: int, sigma: float = 1.0) -> torch.Tensor:
+    """x as a contiguous CPU torch tensor of the given type (RNE cast)."""
+    return torch.from_numpy(draw_rows(rows, cols, seed, sigma)).to(DTYPES[dtype]).contiguous()

@@ -12,6 +12,10 @@ oracle's throughput on a bounded sample of the same workload.
 --window W times attn_fwd_window (sliding window, key j kept for query i only if
 i - W < j, and j < i + W when not causal) and credits 4*d FLOPs per kept pair.
 
+--workload softmax_rows4096_cols32768_f32 (or another softmax workload) times the
+standalone row softmax instead: effective bandwidth in GB/s, counting x read
+once and y written once, against the 8 TB/s HBM roofline.
+
 Traffic calibration (run each under rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE):
     python bench.py --copy-calibration          # plain 256 MiB copy kernel, known bytes
     python bench.py --traffic-summary ATTN_FETCH ATTN_WRITE COPY_FETCH COPY_WRITE
@@ -32,16 +36,19 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak, causal N=4096 d=128"
 METRIC_WINDOW = "sliding-window attention fwd TFLOP/s (4*d per kept query-key pair) and % of bf16 MFMA peak"
+METRIC_SOFTMAX = "row softmax effective bandwidth GB/s (x read once + y written once)"
 MFMA_PEAK_TFLOPS = 2516.6      # dense fp16/bf16: 256 CU x 4096 FLOP/clk x 2.4 GHz (the 2.5 PFLOP/s figure)
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 KERNEL_SOURCE = os.path.join(ROOT, "exact_tiled_attention_03_amd", "csrc", "attn_fwd.hip")
+SOFTMAX_SOURCE = os.path.join(ROOT, "exact_tiled_attention_03_amd", "csrc", "softmax_rows.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def source_hash() -> str:
-    """Hash of the kernel source's code: comments and whitespace are dropped, so that
+def source_hash(path: str = KERNEL_SOURCE) -> str:
+    """Hash of a kernel source's code: comments and whitespace are dropped, so that
     editing a comment does not invalidate counters taken on the same code."""
     import re
-    with open(KERNEL_SOURCE) as f:
+    with open(path) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
@@ -49,11 +56,14 @@ def source_hash() -> str:
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
-def traffic_key(workload: str, causal: int, window: int = 0) -> str:
+def traffic_key(workload: str, causal, window: int = 0) -> str:
+    """Attention entries carry their mask (causal flag, window); the softmax has none."""
+    if causal is None:
+        return workload
     return f"{workload}-causal{causal}" + (f"-window{window}" if window > 0 else "")
 
 
-def measured_traffic(workload: str, causal: int, window: int = 0):
+def measured_traffic(workload: str, causal: int, window: int = 0, source: str = KERNEL_SOURCE):
     """HBM bytes per launch from the committed rocprofv3 counter runs, or None when
     absent or when the kernel source changed since they were taken."""
     try:
@@ -62,7 +72,7 @@ def measured_traffic(workload: str, causal: int, window: int = 0):
     except (OSError, ValueError):
         return None
     entry = t.get(traffic_key(workload, causal, window))
-    if not entry or entry.get("source_sha256_16") != source_hash():
+    if not entry or entry.get("source_sha256_16") != source_hash(source):
         return None
     return entry.get("bytes_per_launch")
 
@@ -94,19 +104,20 @@ def _pmc_kib_per_dispatch(directory: str, counter: str, kernel_substr: str) -> f
     return statistics.median(vals.values())
 
 
-def traffic_summary(attn_fetch, attn_write, copy_fetch, copy_write, workload, causal, window=0):
-    """HBM bytes per attention launch: FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by
+def traffic_summary(attn_fetch, attn_write, copy_fetch, copy_write, workload, causal, window=0,
+                    kernel_substr="attn_fwd_kernel", source=KERNEL_SOURCE):
+    """HBM bytes per kernel launch: FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by
     the ratio of known bytes to what the same counter reads for the plain copy kernel."""
     f_copy = _pmc_kib_per_dispatch(copy_fetch, "FETCH_SIZE", "elementwise") * 1024
     w_copy = _pmc_kib_per_dispatch(copy_write, "WRITE_SIZE", "elementwise") * 1024
-    f_attn = _pmc_kib_per_dispatch(attn_fetch, "FETCH_SIZE", "attn_fwd_kernel") * 1024
-    w_attn = _pmc_kib_per_dispatch(attn_write, "WRITE_SIZE", "attn_fwd_kernel") * 1024
+    f_attn = _pmc_kib_per_dispatch(attn_fetch, "FETCH_SIZE", kernel_substr) * 1024
+    w_attn = _pmc_kib_per_dispatch(attn_write, "WRITE_SIZE", kernel_substr) * 1024
     f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
     entry = {"bytes_per_launch": round(f_attn * f_scale + w_attn * w_scale),
              "read_bytes": round(f_attn * f_scale), "written_bytes": round(w_attn * w_scale),
              "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
              "raw_fetch_kib": f_attn / 1024, "raw_write_kib": w_attn / 1024,
-             "source_sha256_16": source_hash()}
+             "source_sha256_16": source_hash(source)}
     try:
         with open(TRAFFIC_FILE) as f:
             table = json.load(f)
@@ -182,6 +193,93 @@ def cpu_baseline(w, causal, q, k, v, out, lse, budget_s: float, window: int = 0)
             "parity_of_timed_output": {"max_abs": max_err, "lse_max_abs": lse_err}}
 
 
+def softmax_cpu_baseline(w, x, y, budget_s: float):
+    """Time the float64 oracle on blocks of 16 rows of the same workload until ~budget_s
+    of CPU work; also re-check the GPU output of those rows against it."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        rows, t_work, max_rel = 0, 0.0, 0.0
+        while rows < w.rows and t_work < budget_s:
+            xc, yc = x[rows:rows + 16].cpu(), y[rows:rows + 16].cpu().double().numpy()
+            t0 = time.perf_counter()
+            ref = oracle.softmax_rows(xc)
+            t_work += time.perf_counter() - t0
+            max_rel = max(max_rel, float((np.abs(yc - ref) / np.maximum(ref, 1e-300)).max()))
+            rows += xc.shape[0]
+    es = 4 if w.dtype == "f32" else 2
+    return {"value": 2.0 * rows * w.cols * es / t_work / 1e9, "unit": "GB/s", "cores": int(blas_threads),
+            "kind": "oracle", "sample": f"{rows} of {w.rows} rows (blocks of 16), all {w.cols} columns each",
+            "seconds": round(t_work, 3), "host_cpus": cores,
+            "parity_of_timed_output": {"max_rel": max_rel}}
+
+
+def bench_softmax(args, w):
+    """One step = one softmax_rows call over the whole [rows, cols] workload."""
+    import torch
+    import attn_workloads as aw
+    import exact_tiled_attention_03_amd as eta
+
+    dev = torch.device("cuda:0")
+    x = aw.make_rows(w.rows, w.cols, w.dtype, w.seed, w.sigma).to(dev)
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        eta.softmax_rows(x, y, stream=stream)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        eta.softmax_rows(x, y, stream=stream)
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+
+    total_ms = t_begin.elapsed_time(t_end)
+    per_launch = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    ms_per_step = total_ms / args.steps
+    launch_ms = statistics.mean(per_launch)
+    nbytes = w.algorithmic_bytes()
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    kernel = "softmax_row_tiled_kernel" if w.cols > 65536 else "softmax_row_kernel"
+    line = {
+        "metric": METRIC_SOFTMAX,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": f"synthetic (seeded iid N(0,{w.sigma:g}) x)",
+        "config": {"workload": w.name, "rows": w.rows, "cols": w.cols, "layout": "[rows, cols] contiguous",
+                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                   "launch_ms_median": round(statistics.median(per_launch), 5),
+                   "launch_ms_min": round(min(per_launch), 5)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(w.name, None, 0, SOFTMAX_SOURCE),
+                     "kernel": kernel, "algorithmic_bytes_per_launch": nbytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = softmax_cpu_baseline(w, x, y, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,6 +297,9 @@ def main():
 
     if args.traffic_summary:
         import attn_workloads as aw
+        if args.workload and args.workload.startswith("softmax_"):
+            traffic_summary(*args.traffic_summary, args.workload, None, 0, "softmax_row", SOFTMAX_SOURCE)
+            return
         w = aw.by_name(args.workload) if args.workload else aw.WORKLOADS[aw.HEADLINE]
         traffic_summary(*args.traffic_summary, w.name, w.causal_modes[0] if args.causal is None else args.causal,
                         args.window)
@@ -218,6 +319,9 @@ def main():
     import attn_workloads as aw
     import exact_tiled_attention_03_amd as eta
 
+    if args.workload and args.workload.startswith("softmax_"):
+        bench_softmax(args, aw.softmax_by_name(args.workload))
+        return
     w = aw.by_name(args.workload) if args.workload else aw.WORKLOADS[aw.HEADLINE]
     causal = w.causal_modes[0] if args.causal is None else args.causal
     dev = torch.device("cuda:0")

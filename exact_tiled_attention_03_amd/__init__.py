@@ -1,7 +1,8 @@
 """Python binding of the fused exact-attention forward library (libattn.so, gfx950).
 
-Argument marshalling only: every step of the forward pass runs in the HIP
-kernels behind the C ABI declared in include/attn.h.  torch is used for
+Argument marshalling only: every step of the forward pass and of the row
+softmax runs in the HIP kernels behind the C ABI declared in include/attn.h and
+include/softmax.h.  torch is used for
 device memory and the current stream.  If the compiled library is missing the
 binding raises; there is no fallback implementation.
 """
@@ -15,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libattn.so")
 
 ATTN_F16 = 0
 ATTN_BF16 = 1
+ATTN_F32 = 2
 ATTN_OK = 0
 
 _lib = None
@@ -22,7 +24,7 @@ _lib = None
 
 class AttnError(RuntimeError):
     def __init__(self, status: int, msg: str):
-        super().__init__(f"attn_fwd failed with status {status}: {msg}")
+        super().__init__(f"call failed with status {status}: {msg}")
         self.status = status
 
 
@@ -46,6 +48,9 @@ def load_library():
                                     ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
     lib.attn_fwd_schedule.restype = ctypes.c_int
     lib.attn_fwd_schedule.argtypes = [ctypes.c_int] * 5
+    lib.softmax_rows.restype = ctypes.c_int
+    lib.softmax_rows.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_longlong,
+                                 ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     _lib = lib
     return lib
 
@@ -63,13 +68,15 @@ def attn_fwd_schedule(B: int, H: int, N: int, d: int, causal: bool) -> int:
     return load_library().attn_fwd_schedule(int(B), int(H), int(N), int(d), int(bool(causal)))
 
 
-def _dtype_code(t):
+def _dtype_code(t, allow_f32=False):
     import torch
     if t.dtype == torch.float16:
         return ATTN_F16
     if t.dtype == torch.bfloat16:
         return ATTN_BF16
-    raise TypeError(f"unsupported dtype {t.dtype}; expected float16 or bfloat16")
+    if allow_f32 and t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float16 or bfloat16" + (" or float32" if allow_f32 else ""))
 
 
 def _stream_handle(stream):
@@ -128,5 +135,39 @@ def attention(q, k, v, causal: bool, scale: float, stream=None, window: int = 0)
     return out, lse
 
 
-__all__ = ["attn_fwd", "attn_fwd_schedule", "attn_status_string", "attention", "load_library", "AttnError",
-           "ATTN_F16", "ATTN_BF16", "ATTN_SCHEDULE_SMALL", "ATTN_SCHEDULE_WIDE"]
+def softmax_rows(x, y=None, stream=None):
+    """Row softmax of a 2-D GPU tensor x (float32, float16 or bfloat16) into y.
+
+    y defaults to a new tensor with x's row stride; y may be x itself (in place).
+    Rows may be strided (stride(1) must be 1); 16-byte aligned row starts take
+    the vectorised kernels.  Enqueued on
+    `stream` (default: torch's current stream); returns y.  An empty x has nothing
+    to compute and returns y at once.  Raises AttnError with the library's status
+    on rejected arguments."""
+    import torch
+    lib = load_library()
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, cols]")
+    if y is None:
+        row = x.stride(0) if x.dim() == 2 and x.shape[0] > 1 and x.stride(1) == 1 else x.shape[-1]
+        y = torch.empty_strided(tuple(x.shape), (max(row, x.shape[-1]), 1), dtype=x.dtype, device=x.device)
+    if tuple(y.shape) != tuple(x.shape) or y.dtype != x.dtype:
+        raise ValueError(f"y must match x: {tuple(x.shape)} {x.dtype}")
+    for name, t in (("x", x), ("y", y)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
+        if t.shape[1] > 1 and t.stride(1) != 1:
+            raise ValueError(f"{name} rows must be contiguous (stride(1) == 1)")
+    rows, cols = x.shape
+    if rows == 0 or cols == 0:
+        return y
+    st = lib.softmax_rows(x.data_ptr(), x.stride(0) if rows > 1 else cols, y.data_ptr(),
+                          y.stride(0) if rows > 1 else cols, rows, cols, _dtype_code(x, allow_f32=True),
+                          _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, attn_status_string(st))
+    return y
+
+
+__all__ = ["attn_fwd", "attn_fwd_schedule", "attn_status_string", "attention", "softmax_rows", "load_library",
+           "AttnError", "ATTN_F16", "ATTN_BF16", "ATTN_F32", "ATTN_SCHEDULE_SMALL", "ATTN_SCHEDULE_WIDE"]

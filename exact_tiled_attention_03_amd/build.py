@@ -7,7 +7,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", "attn_fwd.hip")]
+SOURCES = [os.path.join(HERE, "csrc", "attn_fwd.hip"), os.path.join(HERE, "csrc", "softmax_rows.hip")]
 OUTPUT = os.path.join(HERE, "libattn.so")
 
 HIPCC_FLAGS = [

@@ -26,14 +26,16 @@
 extern "C" {
 #endif
 
-/* Element type of q, k, v and out. */
+/* Element type of q, k, v and out (and of softmax_rows' x and y). */
 typedef enum {
     ATTN_F16 = 0,  /* IEEE binary16 */
-    ATTN_BF16 = 1  /* bfloat16 */
+    ATTN_BF16 = 1, /* bfloat16 */
+    ATTN_F32 = 2   /* IEEE binary32: softmax_rows only; attn_fwd rejects it */
 } attn_dtype;
 
 /* Return codes.  On any code other than ATTN_OK nothing has been written and
- * nothing has been launched, except ATTN_ERR_LAUNCH (the launch itself failed). */
+ * nothing has been launched, except ATTN_ERR_LAUNCH (the launch itself failed).
+ * The notes give attn_fwd's causes; softmax.h states softmax_rows' own. */
 typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,      /* q, k, v or out is NULL */

@@ -12,6 +12,8 @@ import exact_tiled_attention_03_amd as eta
 from conftest import ROOT, gpu_available
 
 HEADER = os.path.join(ROOT, "include", "attn.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 
 @pytest.fixture(scope="module")
@@ -22,10 +24,13 @@ def lib():
     return eta.load_library()
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(attn_\w+)\s*\(", text, flags=re.M)))
+def declared_functions(headers=None):
+    """Function names declared (outside comments) in the given headers, default all of include/*.h."""
+    names = set()
+    for h in headers or HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_]\w*)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def declared_enum(name_prefix):
@@ -34,7 +39,9 @@ def declared_enum(name_prefix):
 
 
 def test_header_declares_entry_points():
-    assert declared_functions() == ["attn_fwd", "attn_fwd_schedule", "attn_fwd_window", "attn_status_string"]
+    assert declared_functions([HEADER]) == ["attn_fwd", "attn_fwd_schedule", "attn_fwd_window", "attn_status_string"]
+    assert declared_functions() == ["attn_fwd", "attn_fwd_schedule", "attn_fwd_window", "attn_status_string",
+                                    "softmax_rows"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -45,6 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_python_constants_match_header():
     enum = declared_enum("ATTN_")
     assert enum["ATTN_F16"] == eta.ATTN_F16 and enum["ATTN_BF16"] == eta.ATTN_BF16
+    assert enum["ATTN_F32"] == eta.ATTN_F32
     assert enum["ATTN_OK"] == eta.ATTN_OK
 
 
@@ -133,3 +141,42 @@ def test_binding_rejects_cpu_tensors():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
     with pytest.raises(ValueError):
         eta.attn_fwd(q, q, q, torch.empty_like(q), None, True, 0.125)
+
+
+# --- softmax_rows (include/softmax.h) -----------------------------------------
+
+def call_softmax(lib, x=A, xs=64, y=A + SZ, ys=64, rows=4, cols=50, dtype=2):
+    return lib.softmax_rows(x, xs, y, ys, rows, cols, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), 1), (dict(y=None), 1),
+    (dict(rows=0), 2), (dict(rows=-3), 2), (dict(cols=0), 2), (dict(xs=49), 2), (dict(ys=10), 2),
+    (dict(xs=1 << 62), 2), (dict(rows=1 << 30, xs=1 << 20), 2),
+    (dict(dtype=3), 4), (dict(dtype=-1), 4),
+    (dict(x=A + 2), 6), (dict(y=A + SZ + 1), 6), (dict(dtype=0, x=A + 1), 6), (dict(dtype=1, y=A + SZ + 3), 6),
+    (dict(y=A + 16), 10), (dict(y=A, ys=128), 10), (dict(y=A + 3 * 64 * 4 + 48), 10),
+])
+def test_softmax_argument_validation(lib, kw, code):
+    assert code != 0   # every case here must fail validation: the fake pointers are never dereferenced
+    assert call_softmax(lib, **kw) == code, eta.attn_status_string(code)
+
+
+def test_softmax_valid_arguments_reach_the_device_check(lib):
+    # valid arguments would launch on the fake pointers where a gfx950 is current
+    if gpu_available():
+        pytest.skip("device check refuses only where no gfx950 is current")
+    for kw in (dict(), dict(y=A), dict(x=A + SZ, y=A), dict(rows=1, cols=1, xs=1 << 20, ys=4), dict(dtype=0, cols=64),
+               dict(dtype=1, cols=1 << 20, xs=1 << 20, ys=1 << 20, y=A + (1 << 23)),
+               dict(y=A + 4 * 64 * 4),   # y starts just past x's last row
+               dict(x=A + 4, xs=63), dict(dtype=0, x=A + 2, xs=51, y=A + SZ + 6)):   # element-aligned rows
+        assert call_softmax(lib, **kw) == 7, kw
+
+
+def test_softmax_binding_rejects_bad_tensors():
+    import torch
+    x = torch.zeros(4, 8)
+    with pytest.raises(ValueError):
+        eta.softmax_rows(x)                       # on the CPU
+    with pytest.raises(ValueError):
+        eta.softmax_rows(torch.zeros(2, 3, 4))    # not 2-D
