@@ -1,9 +1,10 @@
-"""CPU float64 oracle for the exact attention forward pass.
+"""CPU float64 oracles: exact attention forward, row softmax, GEMM + bias + activation.
 
 TEST INFRASTRUCTURE ONLY: used by tests/, the smoke check and the benchmark's
 CPU-baseline leg.  The HIP library never imports it.
 """
 from .attention import attention, softmax_weights
 from .softmax import softmax_rows
+from .gemm import gemm_bias_act
 
-__all__ = ["attention", "softmax_weights", "softmax_rows"]
+__all__ = ["attention", "softmax_weights", "softmax_rows", "gemm_bias_act"]
