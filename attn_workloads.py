@@ -1,9 +1,10 @@
-"""Seeded synthetic workloads for the attention forward pass and the row softmax.
+"""Seeded synthetic workloads for the attention forward pass, the row softmax and
+the matrix product with its fused epilogue.
 
 This module is shared by the tests, the benchmark and smoke check.  It draws
 inputs and sample rows and holds the table of workload shapes; it contains none
-of the attention or softmax arithmetic, so neither the CPU oracle nor the HIP
-library depends on the other through it.
+of the attention, softmax or matrix-product arithmetic, so neither the CPU
+oracle nor the HIP library depends on the other through it.
 
 Recipe (identical for every consumer):
   * numpy ``default_rng(seed)``, seed = 1000 + workload index;
@@ -175,3 +176,75 @@ def draw_rows(rows: int, cols: int, seed: int, sigma: float = 1.0) -> np.ndarray
 def make_rows(rows: int, cols: int, dtype: str, seed: int, sigma: float = 1.0) -> torch.Tensor:
     """x as a contiguous CPU torch tensor of the given type (RNE cast)."""
     return torch.from_numpy(draw_rows(rows, cols, seed, sigma)).to(DTYPES[dtype]).contiguous()
+
+
+# --- matrix product with bias and activation -------------------------------------
+#
+# Recipe: numpy default_rng(seed); A drawn as iid N(0, 1) float32 [M, K], then
+# B as iid N(0, 1/K) float32 (stored [K, N], or [N, K] for the weight layout),
+# then bias as iid N(0, 1) float32 [N]; each cast to the workload's type by
+# torch on the CPU (round to nearest even).  The shapes are the projections on
+# either side of the attention workload B=2 H=32 N=4096 d=128: 8192 tokens of
+# model width 4096, the fused Q/K/V projection to 3 x 4096 and an MLP
+# up-projection to 4 x 4096 with tanh-GELU, plus the pages' K x N layout with
+# ReLU ("CS336 Lecture 6", Level 3).
+
+
+@dataclass(frozen=True)
+class GemmWorkload:
+    name: str
+    M: int
+    N: int
+    K: int
+    dtype: str          # "fp16" | "bf16"
+    b_layout: str       # "kn" (B stored K x N) | "nk" (weight W stored N x K, B = W^T)
+    act: str            # "none" | "relu" | "gelu_tanh"
+    bias: bool
+    seed: int
+    note: str = field(default="", compare=False)
+
+    def flops(self) -> float:
+        """2 M N K for the product (the epilogue is not counted)."""
+        return 2.0 * self.M * self.N * self.K
+
+    def algorithmic_bytes(self) -> int:
+        """A, B (and bias) read once, C written once."""
+        return 2 * (self.M * self.K + self.K * self.N + self.M * self.N + (self.N if self.bias else 0))
+
+
+GEMM_WORKLOADS = [
+    GemmWorkload("gemm_qkv_m8192_n12288_k4096_bf16", 8192, 12288, 4096, "bf16", "nk", "none", True, 3000,
+                 note="fused Q/K/V projection of 8192 tokens, width 4096"),
+    GemmWorkload("gemm_mlp_m8192_n16384_k4096_bf16_gelu", 8192, 16384, 4096, "bf16", "nk", "gelu_tanh", True, 3001,
+                 note="MLP up-projection with tanh-GELU"),
+    GemmWorkload("gemm_kn_m4096_n4096_k4096_fp16_relu", 4096, 4096, 4096, "fp16", "kn", "relu", True, 3002,
+                 note="the pages' K x N layout with the fused ReLU"),
+]
+
+
+def gemm_by_name(name: str) -> GemmWorkload:
+    for w in GEMM_WORKLOADS:
+        if w.name == name:
+            return w
+    raise KeyError(name)
+
+
+def draw_gemm(M: int, N: int, K: int, b_layout: str, seed: int):
+    """(A, B, bias) as float32 numpy arrays following the recipe above; B is returned
+    in its storage layout ([K, N] for "kn", [N, K] for "nk")."""
+    rng = np.random.default_rng(seed)
+    a = rng.standard_normal((M, K), dtype=np.float32)
+    shape = (K, N) if b_layout == "kn" else (N, K)
+    b = rng.standard_normal(shape, dtype=np.float32) * np.float32(1.0 / math.sqrt(max(K, 1)))
+    bias = rng.standard_normal(N, dtype=np.float32)
+    return a, b, bias
+
+
+def make_gemm(M: int, N: int, K: int, dtype: str, b_layout: str, seed: int):
+    """(A, B, bias) as contiguous CPU torch tensors of the given 16-bit type (RNE cast)."""
+    tdt = DTYPES[dtype]
+    return tuple(torch.from_numpy(x).to(tdt).contiguous() for x in draw_gemm(M, N, K, b_layout, seed))
+
+
+def gemm_workload_inputs(w: GemmWorkload):
+    return make_gemm(w.M, w.N, w.K, w.dtype, w.b_layout, w.seed)

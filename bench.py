@@ -16,6 +16,10 @@ i - W < j, and j < i + W when not causal) and credits 4*d FLOPs per kept pair.
 standalone row softmax instead: effective bandwidth in GB/s, counting x read
 once and y written once, against the 8 TB/s HBM roofline.
 
+--workload gemm_qkv_m8192_n12288_k4096_bf16 (or another gemm workload) times the
+matrix product with its fused bias + activation epilogue: TFLOP/s counting
+2*M*N*K, against the dense bf16/fp16 MFMA peak.
+
 Traffic calibration (run each under rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE):
     python bench.py --copy-calibration          # plain 256 MiB copy kernel, known bytes
     python bench.py --traffic-summary ATTN_FETCH ATTN_WRITE COPY_FETCH COPY_WRITE
@@ -41,6 +45,8 @@ MFMA_PEAK_TFLOPS = 2516.6      # dense fp16/bf16: 256 CU x 4096 FLOP/clk x 2.4 G
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 KERNEL_SOURCE = os.path.join(ROOT, "exact_tiled_attention_03_amd", "csrc", "attn_fwd.hip")
 SOFTMAX_SOURCE = os.path.join(ROOT, "exact_tiled_attention_03_amd", "csrc", "softmax_rows.hip")
+GEMM_SOURCE = os.path.join(ROOT, "exact_tiled_attention_03_amd", "csrc", "gemm.hip")
+METRIC_GEMM = "GEMM + bias + activation TFLOP/s (2*M*N*K) and % of bf16 MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -280,6 +286,99 @@ def bench_softmax(args, w):
     print(json.dumps(line), flush=True)
 
 
+def gemm_cpu_baseline(w, a, b, bias, c, budget_s: float):
+    """Time the float64 oracle on blocks of 8 rows of A (all of B) until ~budget_s of
+    CPU work; also re-check the GPU output of those rows against it."""
+    import numpy as np
+    from oracle import gemm as og
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    acts = {"none": og.ACT_NONE, "relu": og.ACT_RELU, "gelu_tanh": og.ACT_GELU_TANH}
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        bl = b.cpu() if w.b_layout == "kn" else b.cpu().t()
+        bc = bias.cpu() if w.bias else None
+        rows, t_work, max_err = 0, 0.0, 0.0
+        while rows < w.M and t_work < budget_s:
+            ac, cc = a[rows:rows + 8].cpu(), c[rows:rows + 8].cpu().double().numpy()
+            t0 = time.perf_counter()
+            ref = og.gemm_bias_act(ac, bl, bc, acts[w.act])
+            t_work += time.perf_counter() - t0
+            max_err = max(max_err, float(np.abs(cc - ref).max()))
+            rows += ac.shape[0]
+    return {"value": 2.0 * rows * w.N * w.K / t_work / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads),
+            "kind": "oracle", "sample": f"{rows} of {w.M} rows of A (blocks of 8) against all of B",
+            "seconds": round(t_work, 3), "host_cpus": cores, "parity_of_timed_output": {"max_abs": max_err}}
+
+
+def bench_gemm(args, w):
+    """One step = one gemm_bias_act call over the whole workload."""
+    import torch
+    import attn_workloads as aw
+    import exact_tiled_attention_03_amd as eta
+
+    dev = torch.device("cuda:0")
+    a, b, bias = (t.to(dev) for t in aw.gemm_workload_inputs(w))
+    bias = bias if w.bias else None
+    c = torch.empty((w.M, w.N), dtype=a.dtype, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        eta.gemm_bias_act(a, b, bias, w.act, w.b_layout, c=c, stream=stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+
+    total_ms = t_begin.elapsed_time(t_end)
+    per_launch = [x.elapsed_time(y) for x, y in zip(starts, ends)]
+    ms_per_step = total_ms / args.steps
+    launch_ms = statistics.mean(per_launch)
+    flops = w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (launch_ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC_GEMM,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded iid N(0,1) A, N(0,1/K) B, N(0,1) bias)",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "b_layout": w.b_layout, "act": w.act,
+                   "bias": w.bias, "pct_of_mfma_peak": round(100 * value / MFMA_PEAK_TFLOPS, 2),
+                   "launch_ms_median": round(statistics.median(per_launch), 5),
+                   "launch_ms_min": round(min(per_launch), 5)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(w.name, None, 0, GEMM_SOURCE),
+                     "kernel": f"gemm_kernel<{w.dtype},{w.b_layout}>",
+                     "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": w.algorithmic_bytes()},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = gemm_cpu_baseline(w, a, b, bias, c, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -299,6 +398,9 @@ def main():
         import attn_workloads as aw
         if args.workload and args.workload.startswith("softmax_"):
             traffic_summary(*args.traffic_summary, args.workload, None, 0, "softmax_row", SOFTMAX_SOURCE)
+            return
+        if args.workload and args.workload.startswith("gemm_"):
+            traffic_summary(*args.traffic_summary, args.workload, None, 0, "gemm_kernel", GEMM_SOURCE)
             return
         w = aw.by_name(args.workload) if args.workload else aw.WORKLOADS[aw.HEADLINE]
         traffic_summary(*args.traffic_summary, w.name, w.causal_modes[0] if args.causal is None else args.causal,
@@ -321,6 +423,9 @@ def main():
 
     if args.workload and args.workload.startswith("softmax_"):
         bench_softmax(args, aw.softmax_by_name(args.workload))
+        return
+    if args.workload and args.workload.startswith("gemm_"):
+        bench_gemm(args, aw.gemm_by_name(args.workload))
         return
     w = aw.by_name(args.workload) if args.workload else aw.WORKLOADS[aw.HEADLINE]
     causal = w.causal_modes[0] if args.causal is None else args.causal

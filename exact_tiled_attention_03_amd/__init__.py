@@ -1,8 +1,8 @@
 """Python binding of the fused exact-attention forward library (libattn.so, gfx950).
 
-Argument marshalling only: every step of the forward pass and of the row
-softmax runs in the HIP kernels behind the C ABI declared in include/attn.h and
-include/softmax.h.  torch is used for
+Argument marshalling only: every step of the forward pass, the row softmax and
+the matrix product with its epilogue runs in the HIP kernels behind the C ABI
+declared in include/attn.h, include/softmax.h and include/gemm.h.  torch is used for
 device memory and the current stream.  If the compiled library is missing the
 binding raises; there is no fallback implementation.
 """
@@ -18,6 +18,10 @@ ATTN_F16 = 0
 ATTN_BF16 = 1
 ATTN_F32 = 2
 ATTN_OK = 0
+
+GEMM_ACT = {"none": 0, "relu": 1, "gelu_tanh": 2}
+GEMM_B_KN = 0
+GEMM_B_NK = 1
 
 _lib = None
 
@@ -48,6 +52,10 @@ def load_library():
                                     ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
     lib.attn_fwd_schedule.restype = ctypes.c_int
     lib.attn_fwd_schedule.argtypes = [ctypes.c_int] * 5
+    lib.gemm_bias_act.restype = ctypes.c_int
+    lib.gemm_bias_act.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.softmax_rows.restype = ctypes.c_int
     lib.softmax_rows.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_longlong,
                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
@@ -169,5 +177,95 @@ def softmax_rows(x, y=None, stream=None):
     return y
 
 
-__all__ = ["attn_fwd", "attn_fwd_schedule", "attn_status_string", "attention", "softmax_rows", "load_library",
+def _row_stride(t, rows):
+    """Elements between rows of a 2-D tensor whose rows are contiguous."""
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("rows must be contiguous (stride(1) == 1)")
+    return t.stride(0) if rows > 1 else t.shape[1]
+
+
+def _aligned(t, rows):
+    """Every row of t starts on a 16-byte boundary."""
+    return t.data_ptr() % 16 == 0 and (rows == 1 or t.stride(0) % 8 == 0)
+
+
+def _padded(t, rows_to, cols_to):
+    """t copied into the top-left corner of a zeroed [rows_to, cols_to] buffer on its device."""
+    import torch
+    out = torch.zeros((rows_to, cols_to), dtype=t.dtype, device=t.device)
+    out[:t.shape[0], :t.shape[1]].copy_(t)
+    return out
+
+
+def gemm_bias_act(a, b, bias=None, act="none", b_layout="kn", c=None, stream=None):
+    """C = act(A B + bias) on the GPU, fp32 accumulation, one rounding to the input type.
+
+    a: [M, K] float16/bfloat16 with contiguous rows.
+    b: [K, N] when b_layout == "kn"; when b_layout == "nk", the [N, K] matrix W
+       whose transpose is B (a linear layer's weight: C = a W^T).
+    bias: [N] of the same dtype, or None.  act: "none", "relu" or "gelu_tanh".
+    c: [M, N] output (allocated when None).  Enqueued on `stream` (default:
+    torch's current stream); returns c.  Raises AttnError with the library's
+    status on rejected arguments.
+
+    The library reads A and B in 16-byte chunks: it needs 16-byte aligned rows
+    and K a multiple of 8.  Operands that do not meet this are first copied on
+    the GPU into zero-padded buffers (padding K with zeros adds nothing to the
+    sum); every arithmetic step still runs in the library's kernel."""
+    import torch
+    lib = load_library()
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be 2-D")
+    if b_layout not in ("kn", "nk"):
+        raise ValueError("b_layout must be 'kn' or 'nk'")
+    M, K = a.shape
+    N = b.shape[1] if b_layout == "kn" else b.shape[0]
+    if (b.shape[0] if b_layout == "kn" else b.shape[1]) != K:
+        raise ValueError(f"inner dimensions differ: a {tuple(a.shape)}, b {tuple(b.shape)} ({b_layout})")
+    if b.dtype != a.dtype or (bias is not None and bias.dtype != a.dtype):
+        raise TypeError("a, b and bias must share a dtype")
+    if bias is not None and (bias.dim() != 1 or bias.shape[0] != N or (N > 1 and bias.stride(0) != 1)):
+        raise ValueError(f"bias must be a contiguous [{N}] vector")
+    if act not in GEMM_ACT:
+        raise ValueError(f"act must be one of {sorted(GEMM_ACT)}")
+    if c is None:
+        c = torch.empty((M, N), dtype=a.dtype, device=a.device)
+    if tuple(c.shape) != (M, N) or c.dtype != a.dtype:
+        raise ValueError(f"c must be [{M}, {N}] of {a.dtype}")
+    for name, t in (("a", a), ("b", b), ("c", c)) + ((("bias", bias),) if bias is not None else ()):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
+    if M == 0 or N == 0:
+        return c
+    if K > 0:
+        _row_stride(a, M)
+        _row_stride(b, K if b_layout == "kn" else N)
+        K8 = -(-K // 8) * 8
+        if K8 != K or not _aligned(a, M):
+            a = _padded(a, M, K8)
+        if b_layout == "kn":
+            if K8 != K or not _aligned(b, K):
+                b = _padded(b, K8, -(-N // 8) * 8)[:, :N]
+        elif K8 != K or not _aligned(b, N):
+            b = _padded(b, N, K8)
+        K = K8
+    lda = _row_stride(a, M) if K > 0 else K
+    brows = K if b_layout == "kn" else N
+    ldb = _row_stride(b, brows) if K > 0 else (N if b_layout == "kn" else K)
+    ldc = _row_stride(c, M)
+    st = lib.gemm_bias_act(a.data_ptr() if K > 0 else None, lda, b.data_ptr() if K > 0 else None, ldb,
+                           GEMM_B_KN if b_layout == "kn" else GEMM_B_NK,
+                           bias.data_ptr() if bias is not None else None, c.data_ptr(), ldc, M, N, K, GEMM_ACT[act],
+                           _dtype_code(a), _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, attn_status_string(st))
+    return c
+
+
+def linear(x, weight, bias=None, act="none", stream=None):
+    """act(x W^T + bias) for x [M, K] and a weight W [N, K] (gemm_bias_act with b_layout 'nk')."""
+    return gemm_bias_act(x, weight, bias, act, "nk", None, stream)
+
+
+__all__ = ["gemm_bias_act", "linear", "GEMM_ACT", "attn_fwd", "attn_fwd_schedule", "attn_status_string", "attention", "softmax_rows", "load_library",
            "AttnError", "ATTN_F16", "ATTN_BF16", "ATTN_F32", "ATTN_SCHEDULE_SMALL", "ATTN_SCHEDULE_WIDE"]

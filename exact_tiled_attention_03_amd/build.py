@@ -7,7 +7,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", "attn_fwd.hip"), os.path.join(HERE, "csrc", "softmax_rows.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("attn_fwd.hip", "softmax_rows.hip", "gemm.hip", "status.cpp")]
 OUTPUT = os.path.join(HERE, "libattn.so")
 
 HIPCC_FLAGS = [
@@ -28,18 +28,37 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every HIP source into libattn.so; returns its path.  Always recompiles."""
-    tmp = OUTPUT + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    """Compile every source into libattn.so; returns its path.  Always recompiles.
+
+    The translation units are compiled to objects in parallel, then linked."""
+    import tempfile
     noise = "is not a recognized feature for this target"
-    err = "\n".join(line for line in res.stderr.splitlines() if noise not in line)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+    with tempfile.TemporaryDirectory(prefix="eta_build_") as tmpdir:
+        procs, objs = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
+            lang = ["-x", "hip"] if src.endswith(".hip") else []
+            flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+            cmd = [hipcc(), *flags, *extra_flags, "-I", os.path.join(ROOT, "include"), *lang, "-c", src, "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+            objs.append(obj)
+        errors = []
+        for src, proc in procs:
+            _, stderr = proc.communicate()
+            err = "\n".join(line for line in stderr.splitlines() if noise not in line)
+            if proc.returncode != 0:
+                errors.append(f"{os.path.basename(src)}: hipcc failed ({proc.returncode}):\n{err}")
+            elif verbose and err.strip():
+                print(err, file=sys.stderr)
+        if errors:
+            raise RuntimeError("\n".join(errors))
+        tmp = OUTPUT + ".tmp"
+        cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"link failed ({res.returncode}):\n{res.stderr}")
     os.replace(tmp, OUTPUT)
     return OUTPUT
 

@@ -635,21 +635,3 @@ extern "C" int attn_fwd_schedule(int B, int H, int N, int d, int causal) {
     if (st != ATTN_OK) return -st;
     return use_wide((long long)B * H, N, causal) ? ATTN_SCHEDULE_WIDE : ATTN_SCHEDULE_SMALL;
 }
-
-extern "C" const char* attn_status_string(int status) {
-    switch (status) {
-        case ATTN_OK: return "success";
-        case ATTN_ERR_NULL: return "q, k, v or out is NULL";
-        case ATTN_ERR_SHAPE: return "B, H and N must be >= 1, the grid must fit in 2^31-1 work-groups and one head in 2 GB";
-        case ATTN_ERR_HEAD_DIM: return "head dim must be 64, 80 or 128";
-        case ATTN_ERR_DTYPE: return "dtype must be ATTN_F16 or ATTN_BF16";
-        case ATTN_ERR_SCALE: return "scale must be finite";
-        case ATTN_ERR_ALIGN: return "q, k, v, out must be 16-byte aligned and lse 4-byte aligned";
-        case ATTN_ERR_DEVICE: return "no current HIP device, or it is not gfx950";
-        case ATTN_ERR_LAUNCH: return "kernel launch failed";
-        case ATTN_ERR_CAUSAL: return "causal must be 0 or 1";
-        case ATTN_ERR_ALIAS: return "out or lse overlaps an input or each other";
-        case ATTN_ERR_WINDOW: return "window must be >= 0";
-        default: return "unknown status";
-    }
-}

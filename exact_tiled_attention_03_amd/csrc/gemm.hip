@@ -1,0 +1,467 @@
+// gemm.hip -- tiled matrix product with a fused bias + activation epilogue for
+// gfx950 (MI355X), and its C ABI.
+//
+// Method: "Triton: CUDA-level operators in Python", example 3, and "CS336
+// Lecture 6", Level 3: a work-group computes one BM x BN tile of C, walking K
+// in BK steps and accumulating in fp32; the element-wise epilogue (bias of
+// "Triton core syntax" 4.4, then ReLU or tanh-GELU) is applied to the finished
+// tile in registers before its single store, so the unactivated product never
+// reaches HBM.  The grouped launch order of example 3 (GROUP_M tile rows
+// share the B panels they load) decides which tile a work-group takes.
+//
+// gfx950 mapping (not taken from the pages, which target NVIDIA tensor cores):
+//
+//  * 256 x 256 tiles, BK = 64, four waves in a 2 x 2 grid, each wave 128 x 128
+//    = 4 x 4 blocks of v_mfma_f32_32x32x16 (16 fp32 accumulators per lane).
+//  * The MFMA produces C^T: the A operand is a 32-row block of B^T (n, k) and
+//    the B operand a 32-column block of A^T (k, m).  In the 32 x 32
+//    accumulator layout a lane then owns one m and runs of 4 consecutive n,
+//    so the epilogue stores 8 contiguous bytes of a C row at a time.
+//  * A and B tiles go from HBM straight into LDS (buffer loads with the LDS
+//    destination), two stages of 64 KB; rows of 128 bytes, 16-byte chunks
+//    XOR-swizzled by row so the operand reads are free of bank conflicts.
+//    B stored K x N (rows of N) is read through the gfx950 transpose load.
+//  * Edges: buffer range checks return zero past the last row of a panel;
+//    16-byte chunks at or past K are redirected out of range, so they read
+//    as zero in both operands; rows and columns past M, N are never stored.
+//  * Work-group ids are dealt round-robin over the 8 XCDs; they are remapped
+//    so that each XCD takes a contiguous run of the grouped order, keeping
+//    the A and B panels its tiles share in its own L2.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "gemm.h"
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <int DT> struct Elem;
+
+template <> struct Elem<ATTN_F16> {
+    static __device__ __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                      0, 0, 0);
+    }
+    // two floats rounded to nearest even, packed low/high
+    static __device__ __forceinline__ unsigned pack2(float lo, float hi) {
+        f16x2_t p;
+        p[0] = (_Float16)lo;
+        p[1] = (_Float16)hi;
+        return __builtin_bit_cast(unsigned, p);
+    }
+    static __device__ __forceinline__ float get(const unsigned char* p) {
+        return (float)*reinterpret_cast<const _Float16*>(p);
+    }
+    static __device__ __forceinline__ void put(unsigned char* p, float v) { *reinterpret_cast<_Float16*>(p) = (_Float16)v; }
+};
+
+template <> struct Elem<ATTN_BF16> {
+    static __device__ __forceinline__ f32x16_t mfma(u32x4_t a, u32x4_t b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                       c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ unsigned pack2(float lo, float hi) {
+        bf16x2_t p;
+        p[0] = (__bf16)lo;
+        p[1] = (__bf16)hi;
+        return __builtin_bit_cast(unsigned, p);
+    }
+    static __device__ __forceinline__ float get(const unsigned char* p) {
+        return __uint_as_float((unsigned)*reinterpret_cast<const unsigned short*>(p) << 16);
+    }
+    static __device__ __forceinline__ void put(unsigned char* p, float v) { *reinterpret_cast<__bf16*>(p) = (__bf16)v; }
+};
+
+// Tile configuration.
+//
+// LDS stage s (s = 0, 1) at s * STAGE holds the A tile (BM rows of m, BK values
+// of k) at AOFF and the B tile at BOFF.  K-contiguous tiles are BM (or BN) rows
+// of 128 bytes; chunk c (8 values of k) of row r sits at c ^ swz(r) with
+// swz(r) = (r / 2) % 8: the 16 rows read by 16 lanes at one logical chunk then
+// cover 16 distinct 16-byte slots of a 256-byte bank line.  B stored K x N is
+// BK rows (k) of BN values of n (512 bytes); its 64-byte granule g of row r
+// sits at g ^ (r % 8), so the transpose reads of 16 lanes (4 rows x 4 granule
+// offsets) spread over the banks.
+struct Cfg {
+    static constexpr int NT = 256;         // threads: 4 waves
+    static constexpr int BM = 256, BN = 256, BK = 64;
+    static constexpr int WM = 128, WN = 128;  // per wave
+    static constexpr int MB = WM / 32, NB = WN / 32;
+    static constexpr int KS = BK / 16;     // MFMA k-steps per stage
+    static constexpr int ROWB = BK * 2;    // bytes per K-contiguous row
+    static constexpr int AOFF = 0;
+    static constexpr int BOFF = BM * ROWB;           // 32 KB
+    static constexpr int STAGE = BOFF + BN * BK * 2; // 64 KB
+    static constexpr int LDS = 2 * STAGE;            // 128 KB
+    static constexpr int ROUNDS = BM * ROWB / (16 * NT);   // direct-load rounds per tile: 8
+    static constexpr int GROUP_M = 8;                // tile rows per group of the launch order
+    static_assert(BN * BK * 2 == BM * ROWB, "both tiles take the same number of load rounds");
+};
+
+struct GemmArgs {
+    const unsigned char* a;
+    const unsigned char* b;
+    const unsigned char* bias;   // may be null
+    unsigned char* c;
+    long long lda, ldb, ldc;     // in bytes
+    int M, N, K;
+    int act;
+    int tm, tn;                  // tile rows (of M) and tile columns (of N)
+    int c_vec;                   // 8-byte C stores allowed (c and ldc 8-byte aligned)
+};
+
+typedef __fp16 lds_v4h_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __attribute__((address_space(3))) lds_v4h_t* lds_v4h_ptr;
+typedef __attribute__((address_space(3))) unsigned char* lds_bytes;
+
+__device__ __forceinline__ u32x4_t lds_read16(unsigned addr) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>((lds_bytes)(size_t)addr);
+}
+
+// 8 bytes through the gfx950 transpose read: within each 16-lane group, lane i
+// receives element (i % 4) of the 8-byte rows addressed by lanes i/4, i/4 + 4,
+// i/4 + 8, i/4 + 12.
+__device__ __forceinline__ u32x2_t lds_read_tr(unsigned addr) {
+    const lds_v4h_t t = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_v4h_ptr)(lds_bytes)(size_t)addr);
+    return __builtin_bit_cast(u32x2_t, t);
+}
+
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+#if defined(__HIP_DEVICE_COMPILE__)
+
+// Work-group id -> (tile row, tile column).  Ids are dealt round-robin over the
+// 8 XCDs; the remap gives XCD x a contiguous range of the grouped order, which
+// walks GROUP_M tile rows column by column (example 3's L2 grouping).
+__device__ __forceinline__ void map_tile(const GemmArgs& g, int& tile_m, int& tile_n) {
+    const int T = g.tm * g.tn;
+    const int L = blockIdx.x;
+    const int xcd = L & 7;
+    const int v = xcd * (T >> 3) + min(xcd, T & 7) + (L >> 3);
+    const int per_group = Cfg::GROUP_M * g.tn;
+    const int first = (v / per_group) * Cfg::GROUP_M;
+    const int gs = min(g.tm - first, Cfg::GROUP_M);
+    const int w = v - (v / per_group) * per_group;
+    tile_m = first + w % gs;
+    tile_n = w / gs;
+}
+
+__device__ __forceinline__ float gelu_tanh(float z) {
+    // tanh(u) = 1 - 2 / (1 + e^(2u)): +-1 at the extremes, no overflow trouble
+    const float u = 0.7978845608028654f * (z + 0.044715f * z * z * z);
+    const float e = __builtin_amdgcn_exp2f(2.0f * kLog2e * u);
+    const float t = 1.0f - 2.0f / (1.0f + e);
+    return 0.5f * z * (1.0f + t);
+}
+
+template <int DT, bool BKN>
+struct Tile {
+    using C = Cfg;
+    using E = Elem<DT>;
+
+    int lane, wave, wn, wm, hf, l32;
+    int m0, n0, rows_a, rows_b;
+    unsigned lds0;
+    unsigned loff_a, loff_b;     // per-lane direct-load offsets of round 0 within a panel
+    unsigned rstep_a, rstep_b;   // bytes between consecutive load rounds (uniform)
+    int kc;                      // logical 16-byte chunk of k this lane loads (K-contiguous tiles)
+    unsigned ra, rb;             // per-lane LDS offsets of the operand reads (row and chunk of k-step 0)
+    unsigned cx;                 // per-lane swizzle term of the chunk index
+    f32x16_t acc[C::NB][C::MB];
+
+    __device__ __forceinline__ void init(const GemmArgs& g, unsigned lds_base, int tile_m, int tile_n) {
+        const int tid = threadIdx.x;
+        lane = tid & 63;
+        wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave: keeps LDS bases scalar
+        wn = wave & 1;
+        wm = wave >> 1;
+        hf = lane >> 5;
+        l32 = lane & 31;
+        lds0 = lds_base;
+        m0 = tile_m * C::BM;
+        n0 = tile_n * C::BN;
+        rows_a = min(C::BM, g.M - m0);
+        rows_b = min(C::BN, g.N - n0);
+        // K-contiguous tiles: load round it, thread tid fills slot it*256 + tid =
+        // (row it*32 + tid/8, physical chunk tid%8), i.e. logical chunk
+        // (tid%8) ^ swz(row) = (tid%8) ^ ((tid/16)%8), the same in every round
+        kc = (tid & 7) ^ ((tid >> 4) & 7);
+        loff_a = (unsigned)((tid >> 3) * g.lda) + (unsigned)(kc * 16);
+        rstep_a = (unsigned)(32 * g.lda);
+        if constexpr (BKN) {
+            // B stored K x N: row k of the tile is 512 bytes = 8 granules of 64
+            // bytes; round it, thread tid fills slot it*256 + tid = (row it*8 +
+            // tid/32, physical 16-byte chunk tid%32), i.e. granule (tid%32)/4 ^
+            // (row % 8) = (tid%32)/4 ^ (tid/32) and chunk tid%4 within it
+            const int gran = ((tid & 31) >> 2) ^ (tid >> 5);
+            loff_b = (unsigned)((tid >> 5) * g.ldb) + (unsigned)(gran * 64 + (tid & 3) * 16);
+            rstep_b = (unsigned)(8 * g.ldb);
+        } else {
+            loff_b = (unsigned)((tid >> 3) * g.ldb) + (unsigned)(kc * 16);
+            rstep_b = (unsigned)(32 * g.ldb);
+        }
+        cx = (unsigned)((l32 >> 1) & 7);
+        ra = (unsigned)(C::AOFF + (wm * C::WM + l32) * C::ROWB);
+        rb = (unsigned)(C::BOFF + (wn * C::WN + l32) * C::ROWB);
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < C::MB; ++mb) acc[nb][mb] = f32x16_t{};
+    }
+
+    // tile j of A and B into the LDS stage at byte offset `stage`
+    __device__ __forceinline__ void issue(const GemmArgs& g, int j, unsigned stage) const {
+        const int k0 = j * C::BK;
+        const int krem = g.K - k0;                      // > 0
+        const unsigned region = lds0 + stage;
+        {
+            const unsigned char* base = g.a + (size_t)m0 * (size_t)g.lda + (size_t)k0 * 2;
+            const int bytes = (int)((rows_a - 1) * g.lda + (long long)krem * 2);
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, 0x00020000);
+            const unsigned vo = kc * 8 < krem ? loff_a : 0x80000000u;   // chunks past K read as zero
+#pragma unroll
+            for (int it = 0; it < C::ROUNDS; ++it) {
+                const unsigned dst = region + C::AOFF + (unsigned)((it * C::NT + wave * 64) * 16);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_bytes)(size_t)dst,
+                                                         16, vo, it * rstep_a, 0, 0);
+            }
+        }
+        if constexpr (BKN) {
+            // rows k0 .. K-1 of B, columns n0 .. N-1: rows past K read as zero
+            // through the range check, columns past N only feed unstored outputs.
+            // The range ends on a whole 16-byte chunk, so a chunk that straddles
+            // column N is read whole (it lies in one aligned 16-byte block of the
+            // last row, so no byte outside a mapped page is touched)
+            const unsigned char* base = g.b + (size_t)k0 * (size_t)g.ldb + (size_t)n0 * 2;
+            const int kr = min(krem, C::BK);
+            const int bytes = (int)((kr - 1) * g.ldb + (((long long)rows_b * 2 + 15) & ~15LL));
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, 0x00020000);
+#pragma unroll
+            for (int it = 0; it < C::ROUNDS; ++it) {
+                const unsigned dst = region + C::BOFF + (unsigned)((it * C::NT + wave * 64) * 16);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_bytes)(size_t)dst,
+                                                         16, loff_b, it * rstep_b, 0, 0);
+            }
+        } else {
+            const unsigned char* base = g.b + (size_t)n0 * (size_t)g.ldb + (size_t)k0 * 2;
+            const int bytes = (int)((rows_b - 1) * g.ldb + (long long)krem * 2);
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, 0x00020000);
+            const unsigned vo = kc * 8 < krem ? loff_b : 0x80000000u;
+#pragma unroll
+            for (int it = 0; it < C::ROUNDS; ++it) {
+                const unsigned dst = region + C::BOFF + (unsigned)((it * C::NT + wave * 64) * 16);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_bytes)(size_t)dst,
+                                                         16, vo, it * rstep_b, 0, 0);
+            }
+        }
+    }
+
+    // operands of k-step s from the stage at `base` (= lds0 + stage offset):
+    // av[nb] is the MFMA A operand (B^T block nb: 32 n x 16 k), bv[mb] the B
+    // operand (A^T block mb: 16 k x 32 m)
+    __device__ __forceinline__ void operands(unsigned base, int s, u32x4_t (&av)[C::NB], u32x4_t (&bv)[C::MB]) const {
+        const unsigned ch = (unsigned)(((2 * s + hf) ^ cx) * 16);
+        if constexpr (BKN) {
+            // k-rows 16 s + 8 hf .. +7 of column n: two transpose reads of 4
+            // k-rows each (lane j of a 16-lane group addresses k-row 16 s + 8 hf
+            // + 4 h + j/4 at columns n .. n+3, n = block + 16 (group % 2) + 4 (j % 4));
+            // the 64-byte granule of row r is swizzled by r % 8
+            const int g16 = lane >> 4, s16 = lane & 15;
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb) {
+                u32x4_t v;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int r = 16 * s + 8 * (g16 >> 1) + 4 * h + (s16 >> 2);
+                    const int n = wn * C::WN + nb * 32 + 16 * (g16 & 1) + 4 * (s16 & 3);
+                    const int gran = (n >> 5) ^ (r & 7);
+                    const u32x2_t t = lds_read_tr(base + C::BOFF + (unsigned)(r * (C::BN * 2) + gran * 64 + (n & 31) * 2));
+                    v[2 * h] = t[0];
+                    v[2 * h + 1] = t[1];
+                }
+                av[nb] = v;
+            }
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb) av[nb] = lds_read16(base + rb + ch + nb * 32 * C::ROWB);
+        }
+#pragma unroll
+        for (int mb = 0; mb < C::MB; ++mb) bv[mb] = lds_read16(base + ra + ch + mb * 32 * C::ROWB);
+    }
+
+    // the tile in the stage at byte offset `stage`: KS k-steps of NB x MB MFMAs,
+    // the operands of step s+1 read while the MFMAs of step s run
+    __device__ __forceinline__ void compute(unsigned stage) {
+        const unsigned base = lds0 + stage;
+        u32x4_t av[2][C::NB], bv[2][C::MB];
+        operands(base, 0, av[0], bv[0]);
+#pragma unroll
+        for (int s = 0; s < C::KS; ++s) {
+            if (s + 1 < C::KS) operands(base, s + 1, av[(s + 1) & 1], bv[(s + 1) & 1]);
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < C::MB; ++mb) acc[nb][mb] = E::mfma(av[s & 1][nb], bv[s & 1][mb], acc[nb][mb]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // bias, activation, rounding and the store of this wave's 128 x 128 block
+    __device__ __forceinline__ void finish(const GemmArgs& g) const {
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) {
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                // accumulator registers 4 gq .. 4 gq + 3 of a lane hold rows
+                // n = nb*32 + 8 gq + 4 hf + (0..3) of C^T, i.e. columns of C
+                const int n = n0 + wn * C::WN + nb * 32 + 8 * gq + 4 * hf;
+                float bias[4] = {0.f, 0.f, 0.f, 0.f};
+                if (g.bias) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (n + j < g.N) bias[j] = E::get(g.bias + (size_t)(n + j) * 2);
+                }
+#pragma unroll
+                for (int mb = 0; mb < C::MB; ++mb) {
+                    const int m = m0 + wm * C::WM + mb * 32 + l32;
+                    if (m >= g.M || n >= g.N) continue;
+                    float v[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        float z = acc[nb][mb][4 * gq + j] + bias[j];
+                        if (g.act == GEMM_ACT_RELU) z = fmaxf(z, 0.f);
+                        else if (g.act == GEMM_ACT_GELU_TANH) z = gelu_tanh(z);
+                        v[j] = z;
+                    }
+                    unsigned char* dst = g.c + (size_t)m * (size_t)g.ldc + (size_t)n * 2;
+                    if (g.c_vec && n + 3 < g.N) {
+                        *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            if (n + j < g.N) E::put(dst + 2 * j, v[j]);
+                    }
+                }
+            }
+        }
+    }
+};
+
+#endif  // __HIP_DEVICE_COMPILE__
+
+template <int DT, bool BKN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(GemmArgs g) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using C = Cfg;
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS];
+    Tile<DT, BKN> t;
+    int tile_m, tile_n;
+    map_tile(g, tile_m, tile_n);
+    t.init(g, (unsigned)(size_t)(lds_bytes)lds, tile_m, tile_n);
+    const int nk = (g.K + C::BK - 1) / C::BK;
+    if (nk > 0) t.issue(g, 0, 0);
+    for (int j = 0; j < nk; ++j) {
+        wait_loads();
+        __syncthreads();
+        if (j + 1 < nk) t.issue(g, j + 1, ((j + 1) & 1) * C::STAGE);
+        t.compute((j & 1) * C::STAGE);
+    }
+    t.finish(g);
+#endif
+}
+
+// --- host side ---------------------------------------------------------------
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_ERR_DEVICE;
+    if (dev < kMaxDevices) {
+        const int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+        if (st == 1) return ATTN_OK;
+        if (st == 2) return ATTN_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_DEVICE;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok ? ATTN_OK : ATTN_ERR_DEVICE;
+}
+
+bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
+
+}  // namespace
+
+extern "C" int gemm_bias_act(const void* a, long long lda, const void* b, long long ldb, int b_layout, const void* bias,
+                             void* c, long long ldc, int M, int N, int K, int act, int dtype, void* stream) {
+    if (!c || (K > 0 && (!a || !b))) return ATTN_ERR_NULL;
+    if (M < 1 || N < 1 || K < 0 || K % 8 != 0) return ATTN_ERR_SHAPE;
+    if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
+    if (b_layout != GEMM_B_KN && b_layout != GEMM_B_NK) return ATTN_ERR_LAYOUT;
+    if (act != GEMM_ACT_NONE && act != GEMM_ACT_RELU && act != GEMM_ACT_GELU_TANH) return ATTN_ERR_LAYOUT;
+    const bool bkn = b_layout == GEMM_B_KN;
+    if (ldc < N) return ATTN_ERR_SHAPE;
+    if (K > 0) {
+        if (lda < K || ldb < (bkn ? N : K)) return ATTN_ERR_SHAPE;
+        // 32-bit buffer offsets: one panel of A (and of B) must span < 2^31 bytes
+        constexpr long long kSpan = 1LL << 31;
+        if (lda > kSpan / (2 * Cfg::BM) || ldb > kSpan / (2 * (bkn ? Cfg::BK : Cfg::BN))) return ATTN_ERR_SHAPE;
+        if (((uintptr_t)a | (uintptr_t)b) % 16 || lda % 8 || ldb % 8) return ATTN_ERR_ALIGN;
+    }
+    if (ldc > (1LL << 40)) return ATTN_ERR_SHAPE;
+    if (((uintptr_t)c | (uintptr_t)bias) % 2) return ATTN_ERR_ALIGN;
+    // c's span must not meet an input's span
+    const uintptr_t c0 = (uintptr_t)c, c1 = c0 + (uintptr_t)(((long long)M - 1) * ldc + N) * 2;
+    if (K > 0) {
+        const uintptr_t a0 = (uintptr_t)a, a1 = a0 + (uintptr_t)(((long long)M - 1) * lda + K) * 2;
+        const long long brows = bkn ? K : N, bcols = bkn ? N : K;
+        const uintptr_t b0 = (uintptr_t)b, b1 = b0 + (uintptr_t)((brows - 1) * ldb + bcols) * 2;
+        if (overlaps(c0, c1, a0, a1) || overlaps(c0, c1, b0, b1)) return ATTN_ERR_ALIAS;
+    }
+    if (bias && overlaps(c0, c1, (uintptr_t)bias, (uintptr_t)bias + (uintptr_t)N * 2)) return ATTN_ERR_ALIAS;
+    const long long tm = ((long long)M + Cfg::BM - 1) / Cfg::BM, tn = ((long long)N + Cfg::BN - 1) / Cfg::BN;
+    if (tm * tn > 0x7fffffffLL) return ATTN_ERR_SHAPE;
+    const int dev_status = check_device();
+    if (dev_status != ATTN_OK) return dev_status;
+
+    GemmArgs g;
+    g.a = static_cast<const unsigned char*>(a);
+    g.b = static_cast<const unsigned char*>(b);
+    g.bias = static_cast<const unsigned char*>(bias);
+    g.c = static_cast<unsigned char*>(c);
+    g.lda = lda * 2;
+    g.ldb = ldb * 2;
+    g.ldc = ldc * 2;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.act = act;
+    g.tm = (int)tm;
+    g.tn = (int)tn;
+    g.c_vec = ((uintptr_t)c % 8 == 0) && (ldc % 4 == 0);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const dim3 grid((unsigned)(tm * tn)), block(Cfg::NT);
+    if (dtype == ATTN_BF16) {
+        if (bkn) hipLaunchKernelGGL((gemm_kernel<ATTN_BF16, true>), grid, block, 0, s, g);
+        else hipLaunchKernelGGL((gemm_kernel<ATTN_BF16, false>), grid, block, 0, s, g);
+    } else {
+        if (bkn) hipLaunchKernelGGL((gemm_kernel<ATTN_F16, true>), grid, block, 0, s, g);
+        else hipLaunchKernelGGL((gemm_kernel<ATTN_F16, false>), grid, block, 0, s, g);
+    }
+    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}

@@ -35,7 +35,8 @@ typedef enum {
 
 /* Return codes.  On any code other than ATTN_OK nothing has been written and
  * nothing has been launched, except ATTN_ERR_LAUNCH (the launch itself failed).
- * The notes give attn_fwd's causes; softmax.h states softmax_rows' own. */
+ * The notes give attn_fwd's causes; softmax.h and gemm.h state those of
+ * softmax_rows and gemm_bias_act. */
 typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,      /* q, k, v or out is NULL */
@@ -48,7 +49,8 @@ typedef enum {
     ATTN_ERR_LAUNCH = 8,    /* the kernel launch returned an error */
     ATTN_ERR_CAUSAL = 9,    /* causal is neither 0 nor 1 */
     ATTN_ERR_ALIAS = 10,    /* out or lse overlaps q, k, v, or each other */
-    ATTN_ERR_WINDOW = 11    /* window is negative */
+    ATTN_ERR_WINDOW = 11,   /* window is negative */
+    ATTN_ERR_LAYOUT = 12    /* gemm_bias_act: b_layout or act is not a listed value */
 } attn_status;
 
 /*

@@ -33,15 +33,15 @@ def declared_functions(headers=None):
     return sorted(names)
 
 
-def declared_enum(name_prefix):
-    text = open(HEADER).read()
+def declared_enum(name_prefix, header=HEADER):
+    text = open(header).read()
     return {m.group(1): int(m.group(2)) for m in re.finditer(rf"\b({name_prefix}\w+)\s*=\s*(\d+)", text)}
 
 
 def test_header_declares_entry_points():
     assert declared_functions([HEADER]) == ["attn_fwd", "attn_fwd_schedule", "attn_fwd_window", "attn_status_string"]
     assert declared_functions() == ["attn_fwd", "attn_fwd_schedule", "attn_fwd_window", "attn_status_string",
-                                    "softmax_rows"]
+                                    "gemm_bias_act", "softmax_rows"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -180,3 +180,56 @@ def test_softmax_binding_rejects_bad_tensors():
         eta.softmax_rows(x)                       # on the CPU
     with pytest.raises(ValueError):
         eta.softmax_rows(torch.zeros(2, 3, 4))    # not 2-D
+
+
+# --- gemm_bias_act (include/gemm.h) ---------------------------------------------
+
+def call_gemm(lib, a=A, lda=64, b=A + SZ, ldb=64, b_layout=1, bias=A + 2 * SZ, c=A + 3 * SZ, ldc=64, M=4, N=5,
+              K=16, act=0, dtype=1):
+    return lib.gemm_bias_act(a, lda, b, ldb, b_layout, bias, c, ldc, M, N, K, act, dtype, None)
+
+
+def test_gemm_enums_match_binding():
+    enum = declared_enum("GEMM_", os.path.join(ROOT, "include", "gemm.h"))
+    assert enum["GEMM_ACT_NONE"] == eta.GEMM_ACT["none"] and enum["GEMM_ACT_RELU"] == eta.GEMM_ACT["relu"]
+    assert enum["GEMM_ACT_GELU_TANH"] == eta.GEMM_ACT["gelu_tanh"]
+    assert enum["GEMM_B_KN"] == eta.GEMM_B_KN and enum["GEMM_B_NK"] == eta.GEMM_B_NK
+    assert declared_enum("ATTN_ERR_")["ATTN_ERR_LAYOUT"] == 12
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(a=None), 1), (dict(b=None), 1), (dict(c=None), 1), (dict(c=None, K=0), 1),
+    (dict(M=0), 2), (dict(N=-1), 2), (dict(K=-8), 2), (dict(K=12), 2), (dict(K=3), 2), (dict(lda=8), 2),
+    (dict(ldb=8), 2), (dict(b_layout=0, ldb=4), 2), (dict(ldc=4), 2), (dict(lda=1 << 23), 2),
+    (dict(b_layout=0, ldb=(1 << 24) + 8), 2), (dict(ldb=1 << 23), 2),
+    (dict(dtype=2), 4), (dict(dtype=-1), 4),
+    (dict(b_layout=2), 12), (dict(b_layout=-1), 12), (dict(act=3), 12), (dict(act=-1), 12),
+    (dict(a=A + 8), 6), (dict(b=A + SZ + 2), 6), (dict(lda=60), 6), (dict(ldb=20), 6),
+    (dict(c=A + 3 * SZ + 1), 6), (dict(bias=A + 2 * SZ + 1), 6),
+    (dict(c=A), 10), (dict(c=A + SZ + 64), 10), (dict(c=A + 2 * SZ - 8), 10), (dict(bias=A + 3 * SZ + 4), 10),
+])
+def test_gemm_argument_validation(lib, kw, code):
+    assert code != 0   # every case here must fail validation: the fake pointers are never dereferenced
+    assert call_gemm(lib, **kw) == code, eta.attn_status_string(code)
+
+
+def test_gemm_valid_arguments_reach_the_device_check(lib):
+    # valid arguments would launch on the fake pointers where a gfx950 is current
+    if gpu_available():
+        pytest.skip("device check refuses only where no gfx950 is current")
+    for kw in (dict(), dict(bias=None), dict(b_layout=0), dict(act=2, dtype=0), dict(a=None, b=None, K=0),
+               dict(M=1 << 20, N=1 << 10, lda=16, ldb=16, ldc=1 << 10, c=A + (1 << 40))):
+        assert call_gemm(lib, **kw) == 7, kw
+
+
+def test_gemm_binding_rejects_bad_tensors():
+    import torch
+    a = torch.zeros(4, 16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        eta.gemm_bias_act(a, torch.zeros(16, 8, dtype=torch.bfloat16))          # on the CPU
+    with pytest.raises(ValueError):
+        eta.gemm_bias_act(a, torch.zeros(15, 8, dtype=torch.bfloat16))          # inner dims differ
+    with pytest.raises(TypeError):
+        eta.gemm_bias_act(a, torch.zeros(16, 8, dtype=torch.float16))           # dtypes differ
+    with pytest.raises(ValueError):
+        eta.gemm_bias_act(a, torch.zeros(16, 8, dtype=torch.bfloat16), act="tanh")
