@@ -16,6 +16,10 @@ i - W < j, and j < i + W when not causal) and credits 4*d FLOPs per kept pair.
 standalone row softmax instead: effective bandwidth in GB/s, counting x read
 once and y written once, against the 8 TB/s HBM roofline.
 
+--backward times attn_bwd (dQ, dK, dV from the saved lse) on the attention
+workload, crediting 2.5x the forward's FLOPs (the five N x N x d products of
+the backward; recomputing S and dP in the dQ kernel is not credited).
+
 --workload gemm_qkv_m8192_n12288_k4096_bf16 (or another gemm workload) times the
 matrix product with its fused bias + activation epilogue: TFLOP/s counting
 2*M*N*K, against the dense bf16/fp16 MFMA peak.
@@ -39,6 +43,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak, causal N=4096 d=128"
+METRIC_BWD = "attention bwd TFLOP/s (2.5x the forward's 4*B*H*N^2*d, halved for causal) and % of bf16 MFMA peak"
 METRIC_WINDOW = "sliding-window attention fwd TFLOP/s (4*d per kept query-key pair) and % of bf16 MFMA peak"
 METRIC_SOFTMAX = "row softmax effective bandwidth GB/s (x read once + y written once)"
 MFMA_PEAK_TFLOPS = 2516.6      # dense fp16/bf16: 256 CU x 4096 FLOP/clk x 2.4 GHz (the 2.5 PFLOP/s figure)
@@ -379,6 +384,103 @@ def bench_gemm(args, w):
     print(json.dumps(line), flush=True)
 
 
+def bench_backward(args, w, causal):
+    """One step = one attn_bwd call (delta, dQ and dK/dV kernels) over the whole workload."""
+    import torch
+    import attn_workloads as aw
+    import exact_tiled_attention_03_amd as eta
+
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in aw.workload_inputs(w))
+    do = aw.make_inputs(w.shape, w.dtype, w.seed + 500)[0].to(dev)
+    out, lse = eta.attention(q, k, v, bool(causal), w.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    delta = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        eta.attn_bwd(q, k, v, out, lse, do, dq, dk, dv, delta, causal=bool(causal), scale=w.scale, stream=stream)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+    per_launch = [x.elapsed_time(y) for x, y in zip(starts, ends)]
+    ms_per_step = total_ms / args.steps
+    launch_ms = statistics.mean(per_launch)
+    flops = 2.5 * w.flops(causal)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (launch_ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC_BWD,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded iid N(0,1) Q, K, V, dO)",
+        "config": {"workload": w.name + "-backward", "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": causal,
+                   "scale": w.scale, "pct_of_mfma_peak": round(100 * value / MFMA_PEAK_TFLOPS, 2),
+                   "launch_ms_median": round(statistics.median(per_launch), 5),
+                   "launch_ms_min": round(min(per_launch), 5),
+                   "note": "one step = the delta, dQ and dK/dV kernels of one attn_bwd call"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_bwd_delta_kernel + attn_bwd_dq_kernel + attn_bwd_dkdv_kernel",
+                     "algorithmic_flops_per_launch": flops},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = backward_cpu_baseline(w, causal, q, k, v, do, dq, dk, dv, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def backward_cpu_baseline(w, causal, q, k, v, do, dq, dk, dv, budget_s: float):
+    """Time the float64 gradient oracle on whole heads until ~budget_s of CPU work; also
+    re-check the GPU gradients of those heads against it."""
+    import numpy as np
+    from oracle import backward as ob
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        heads, t_work, max_err = 0, 0.0, 0.0
+        for idx in range(w.B * w.H):
+            b, h = divmod(idx, w.H)
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            args_ = [t[sl].cpu() for t in (q, k, v, do)]
+            t0 = time.perf_counter()
+            ref = ob.attention_bwd(*args_, causal, w.scale)
+            t_work += time.perf_counter() - t0
+            for g, r in zip((dq, dk, dv), ref):
+                max_err = max(max_err, float(np.abs(g[sl].cpu().double().numpy() - r).max()))
+            heads += 1
+            if t_work >= budget_s:
+                break
+    flops = 2.5 * w.flops(causal) / (w.B * w.H) * heads
+    return {"value": flops / t_work / 1e12, "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.H} heads, all {w.N} rows each", "seconds": round(t_work, 3),
+            "host_cpus": cores, "parity_of_timed_output": {"max_abs": max_err}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -388,6 +490,7 @@ def main():
     ap.add_argument("--causal", type=int, default=None)
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window W >= 1 (attn_fwd_window); FLOPs then count kept pairs x 4d")
+    ap.add_argument("--backward", action="store_true", help="time attn_bwd on the attention workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -429,6 +532,9 @@ def main():
         return
     w = aw.by_name(args.workload) if args.workload else aw.WORKLOADS[aw.HEADLINE]
     causal = w.causal_modes[0] if args.causal is None else args.causal
+    if args.backward:
+        bench_backward(args, w, causal)
+        return
     dev = torch.device("cuda:0")
     q, k, v = (t.to(dev) for t in aw.workload_inputs(w))
     out = torch.empty_like(q)

@@ -1,8 +1,9 @@
 """Python binding of the fused exact-attention forward library (libattn.so, gfx950).
 
-Argument marshalling only: every step of the forward pass, the row softmax and
-the matrix product with its epilogue runs in the HIP kernels behind the C ABI
-declared in include/attn.h, include/softmax.h and include/gemm.h.  torch is used for
+Argument marshalling only: every step of the forward and backward passes, the
+merge of key-sharded results, the row softmax and the matrix product with its
+epilogue runs in the HIP kernels behind the C ABI declared in include/attn.h,
+include/attn_bwd.h, include/softmax.h and include/gemm.h.  torch is used for
 device memory and the current stream.  If the compiled library is missing the
 binding raises; there is no fallback implementation.
 """
@@ -52,6 +53,12 @@ def load_library():
                                     ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
     lib.attn_fwd_schedule.restype = ctypes.c_int
     lib.attn_fwd_schedule.argtypes = [ctypes.c_int] * 5
+    lib.attn_bwd.restype = ctypes.c_int
+    lib.attn_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int,
+                                                                           ctypes.c_void_p]
+    lib.attn_lse_merge.restype = ctypes.c_int
+    lib.attn_lse_merge.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.gemm_bias_act.restype = ctypes.c_int
     lib.gemm_bias_act.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_int,
@@ -177,6 +184,72 @@ def softmax_rows(x, y=None, stream=None):
     return y
 
 
+def attn_bwd(q, k, v, out, lse, dout, dq=None, dk=None, dv=None, delta=None, causal=True, scale=None,
+             stream=None):
+    """Gradients (dq, dk, dv) of attn_fwd for the upstream gradient dout.
+
+    q, k, v, out, dout: contiguous [B, H, N, d] float16/bfloat16 GPU tensors (out
+    and lse as attn_fwd returned them); lse: contiguous [B, H, N] float32.
+    dq, dk, dv: outputs like q (allocated when None); delta: [B, H, N] float32
+    workspace that receives D_i = sum_c dout * out (allocated when None).
+    scale defaults to 1/sqrt(d).  Returns (dq, dk, dv, delta)."""
+    import math
+    import torch
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
+    for name, t in (("k", k), ("v", v), ("out", out), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be [B, H, N, d] of {q.dtype}")
+    for name, t in (("lse", lse), ("delta", delta)):
+        if tuple(t.shape) != (B, H, N) or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32 [B, H, N]")
+    for t in (q, k, v, out, lse, dout, dq, dk, dv, delta):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous GPU tensors")
+    st = lib.attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, int(bool(causal)),
+                      float(scale), _dtype_code(q), _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, attn_status_string(st))
+    return dq, dk, dv, delta
+
+
+def attn_lse_merge(o_parts, lse_parts, o=None, lse=None, stream=None):
+    """Merge G partial attention results over disjoint key shards.
+
+    o_parts: contiguous [G, ..., d] float16/bfloat16; lse_parts: contiguous
+    [G, ...] float32 (natural log, -inf for a shard with no key for a row).
+    Returns (o [..., d], lse [...])."""
+    import torch
+    lib = load_library()
+    G = o_parts.shape[0]
+    d = o_parts.shape[-1]
+    rows_shape = tuple(o_parts.shape[1:-1])
+    if tuple(lse_parts.shape) != (G,) + rows_shape or lse_parts.dtype != torch.float32:
+        raise ValueError("lse_parts must be float32 [G, ...] matching o_parts")
+    o = torch.empty(rows_shape + (d,), dtype=o_parts.dtype, device=o_parts.device) if o is None else o
+    lse = torch.empty(rows_shape, dtype=torch.float32, device=o_parts.device) if lse is None else lse
+    for t in (o_parts, lse_parts, o, lse):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous GPU tensors")
+    R = 1
+    for x in rows_shape:
+        R *= x
+    st = lib.attn_lse_merge(o_parts.data_ptr(), lse_parts.data_ptr(), G, o.data_ptr(), lse.data_ptr(), R, d,
+                            _dtype_code(o_parts), _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, attn_status_string(st))
+    return o, lse
+
+
 def _row_stride(t, rows):
     """Elements between rows of a 2-D tensor whose rows are contiguous."""
     if t.shape[1] > 1 and t.stride(1) != 1:
@@ -267,5 +340,5 @@ def linear(x, weight, bias=None, act="none", stream=None):
     return gemm_bias_act(x, weight, bias, act, "nk", None, stream)
 
 
-__all__ = ["gemm_bias_act", "linear", "GEMM_ACT", "attn_fwd", "attn_fwd_schedule", "attn_status_string", "attention", "softmax_rows", "load_library",
+__all__ = ["attn_bwd", "attn_lse_merge", "gemm_bias_act", "linear", "GEMM_ACT", "attn_fwd", "attn_fwd_schedule", "attn_status_string", "attention", "softmax_rows", "load_library",
            "AttnError", "ATTN_F16", "ATTN_BF16", "ATTN_F32", "ATTN_SCHEDULE_SMALL", "ATTN_SCHEDULE_WIDE"]

@@ -7,7 +7,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("attn_fwd.hip", "softmax_rows.hip", "gemm.hip", "status.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("attn_fwd.hip", "attn_bwd.hip", "lse_merge.hip", "softmax_rows.hip", "gemm.hip",
+                                                    "status.cpp")]
 OUTPUT = os.path.join(HERE, "libattn.so")
 
 HIPCC_FLAGS = [

@@ -40,8 +40,8 @@ def declared_enum(name_prefix, header=HEADER):
 
 def test_header_declares_entry_points():
     assert declared_functions([HEADER]) == ["attn_fwd", "attn_fwd_schedule", "attn_fwd_window", "attn_status_string"]
-    assert declared_functions() == ["attn_fwd", "attn_fwd_schedule", "attn_fwd_window", "attn_status_string",
-                                    "gemm_bias_act", "softmax_rows"]
+    assert declared_functions() == ["attn_bwd", "attn_fwd", "attn_fwd_schedule", "attn_fwd_window",
+                                    "attn_lse_merge", "attn_status_string", "gemm_bias_act", "softmax_rows"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -233,3 +233,46 @@ def test_gemm_binding_rejects_bad_tensors():
         eta.gemm_bias_act(a, torch.zeros(16, 8, dtype=torch.float16))           # dtypes differ
     with pytest.raises(ValueError):
         eta.gemm_bias_act(a, torch.zeros(16, 8, dtype=torch.bfloat16), act="tanh")
+
+
+# --- attn_bwd, attn_lse_merge (include/attn_bwd.h) ---------------------------------
+
+def call_bwd(lib, **kw):
+    a = dict(q=A, k=A + SZ, v=A + 2 * SZ, out=A + 3 * SZ, lse=A + 4 * SZ, dout=A + 5 * SZ, dq=A + 6 * SZ,
+             dk=A + 7 * SZ, dv=A + 8 * SZ, delta=A + 9 * SZ, B=1, H=2, N=16, d=64, causal=1, scale=0.125, dtype=1)
+    a.update(kw)
+    return lib.attn_bwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"], a["delta"],
+                        a["B"], a["H"], a["N"], a["d"], a["causal"], a["scale"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(lse=None), 1), (dict(dout=None), 1), (dict(dv=None), 1), (dict(delta=None), 1),
+    (dict(B=0), 2), (dict(N=0), 2), (dict(d=96), 3), (dict(dtype=2), 4), (dict(scale=math.nan), 5),
+    (dict(q=A + 8), 6), (dict(dk=A + 7 * SZ + 2), 6), (dict(delta=A + 9 * SZ + 2), 6), (dict(causal=3), 9),
+    (dict(dq=A + 64), 10), (dict(dv=A + 6 * SZ + 16), 10), (dict(delta=A + 8 * SZ), 10), (dict(dk=A + 5 * SZ), 10),
+])
+def test_bwd_argument_validation(lib, kw, code):
+    assert code != 0   # every case must fail validation: the fake pointers are never dereferenced
+    assert call_bwd(lib, **kw) == code, eta.attn_status_string(code)
+
+
+def call_merge(lib, op=A, lp=A + SZ, G=3, o=A + 2 * SZ, lse=A + 3 * SZ, R=100, d=128, dtype=1):
+    return lib.attn_lse_merge(op, lp, G, o, lse, R, d, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(op=None), 1), (dict(lse=None), 1), (dict(G=0), 2), (dict(R=0), 2), (dict(d=96), 3), (dict(dtype=2), 4),
+    (dict(op=A + 8), 6), (dict(lse=A + 3 * SZ + 2), 6), (dict(o=A + 64), 10), (dict(lse=A + SZ + 4), 10),
+    (dict(o=A + 3 * SZ - 16), 10),
+])
+def test_merge_argument_validation(lib, kw, code):
+    assert code != 0
+    assert call_merge(lib, **kw) == code, eta.attn_status_string(code)
+
+
+def test_bwd_and_merge_valid_arguments_reach_the_device_check(lib):
+    # valid arguments would launch on the fake pointers where a gfx950 is current
+    if gpu_available():
+        pytest.skip("device check refuses only where no gfx950 is current")
+    assert call_bwd(lib) == 7 and call_bwd(lib, causal=0, d=80, scale=-0.3) == 7
+    assert call_merge(lib) == 7 and call_merge(lib, G=1, R=1, d=64) == 7
