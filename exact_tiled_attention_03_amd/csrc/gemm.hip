@@ -95,21 +95,37 @@ template <> struct Elem<ATTN_BF16> {
 // BK rows (k) of BN values of n (512 bytes); its 64-byte granule g of row r
 // sits at g ^ (r % 8), so the transpose reads of 16 lanes (4 rows x 4 granule
 // offsets) spread over the banks.
+#ifndef ETA_GEMM_GROUP_M
+#define ETA_GEMM_GROUP_M 4
+#endif
+
+// WAVES waves per work-group in a WAVES_N (along n) x WAVES / WAVES_N (along m)
+// grid; K in steps of BK (64 or 32) through STAGES LDS stages
+template <int WAVES_, int WAVES_N_, int BK_, int STAGES_>
 struct Cfg {
-    static constexpr int NT = 256;         // threads: 4 waves
-    static constexpr int BM = 256, BN = 256, BK = 64;
-    static constexpr int WM = 128, WN = 128;  // per wave
+    static constexpr int WAVES = WAVES_, WAVES_N = WAVES_N_, STAGES = STAGES_;
+    static constexpr int NT = 64 * WAVES;
+    static constexpr int BM = 256, BN = 256, BK = BK_;
+    static constexpr int WN = BN / WAVES_N, WM = BM / (WAVES / WAVES_N);   // per wave
     static constexpr int MB = WM / 32, NB = WN / 32;
     static constexpr int KS = BK / 16;     // MFMA k-steps per stage
     static constexpr int ROWB = BK * 2;    // bytes per K-contiguous row
+    static constexpr int CPRK = BK / 8;    // 16-byte chunks per K-contiguous row
+    static constexpr int RPL = 256 / ROWB; // K-contiguous rows per 256-byte bank line
     static constexpr int AOFF = 0;
-    static constexpr int BOFF = BM * ROWB;           // 32 KB
-    static constexpr int STAGE = BOFF + BN * BK * 2; // 64 KB
-    static constexpr int LDS = 2 * STAGE;            // 128 KB
-    static constexpr int ROUNDS = BM * ROWB / (16 * NT);   // direct-load rounds per tile: 8
-    static constexpr int GROUP_M = 8;                // tile rows per group of the launch order
+    static constexpr int BOFF = BM * ROWB;
+    static constexpr int STAGE = BOFF + BN * BK * 2;
+    static constexpr int LDS = STAGES * STAGE;
+    static constexpr int ROUNDS = BM * ROWB / (16 * NT);   // direct-load rounds per tile (A and B alike)
+    static constexpr int LOADS = 2 * ROUNDS;               // direct loads per tile and wave
+    static constexpr int GROUP_M = ETA_GEMM_GROUP_M; // tile rows per group of the launch order
+    static_assert(BK == 32 || BK == 64, "k step");
     static_assert(BN * BK * 2 == BM * ROWB, "both tiles take the same number of load rounds");
+    static_assert(WAVES % WAVES_N == 0 && WM % 32 == 0 && WN % 32 == 0, "wave layouts");
+    static_assert((NT / CPRK / RPL) % CPRK == 0 && (NT / 32) % 8 == 0, "load rounds keep every lane's swizzle");
+    static_assert(LDS <= 160 * 1024, "LDS");
 };
+using Shape = Cfg<4, 2, 64, 2>;   // the tile shape (BM, BN, GROUP_M) shared by every configuration
 
 struct GemmArgs {
     const unsigned char* a;
@@ -139,7 +155,6 @@ __device__ __forceinline__ u32x2_t lds_read_tr(unsigned addr) {
     return __builtin_bit_cast(u32x2_t, t);
 }
 
-__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 #if defined(__HIP_DEVICE_COMPILE__)
 
@@ -151,9 +166,9 @@ __device__ __forceinline__ void map_tile(const GemmArgs& g, int& tile_m, int& ti
     const int L = blockIdx.x;
     const int xcd = L & 7;
     const int v = xcd * (T >> 3) + min(xcd, T & 7) + (L >> 3);
-    const int per_group = Cfg::GROUP_M * g.tn;
-    const int first = (v / per_group) * Cfg::GROUP_M;
-    const int gs = min(g.tm - first, Cfg::GROUP_M);
+    const int per_group = Shape::GROUP_M * g.tn;
+    const int first = (v / per_group) * Shape::GROUP_M;
+    const int gs = min(g.tm - first, Shape::GROUP_M);
     const int w = v - (v / per_group) * per_group;
     tile_m = first + w % gs;
     tile_n = w / gs;
@@ -167,9 +182,8 @@ __device__ __forceinline__ float gelu_tanh(float z) {
     return 0.5f * z * (1.0f + t);
 }
 
-template <int DT, bool BKN>
+template <int DT, bool BKN, class C>
 struct Tile {
-    using C = Cfg;
     using E = Elem<DT>;
 
     int lane, wave, wn, wm, hf, l32;
@@ -186,8 +200,8 @@ struct Tile {
         const int tid = threadIdx.x;
         lane = tid & 63;
         wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave: keeps LDS bases scalar
-        wn = wave & 1;
-        wm = wave >> 1;
+        wn = wave % C::WAVES_N;
+        wm = wave / C::WAVES_N;
         hf = lane >> 5;
         l32 = lane & 31;
         lds0 = lds_base;
@@ -195,25 +209,25 @@ struct Tile {
         n0 = tile_n * C::BN;
         rows_a = min(C::BM, g.M - m0);
         rows_b = min(C::BN, g.N - n0);
-        // K-contiguous tiles: load round it, thread tid fills slot it*256 + tid =
-        // (row it*32 + tid/8, physical chunk tid%8), i.e. logical chunk
-        // (tid%8) ^ swz(row) = (tid%8) ^ ((tid/16)%8), the same in every round
-        kc = (tid & 7) ^ ((tid >> 4) & 7);
-        loff_a = (unsigned)((tid >> 3) * g.lda) + (unsigned)(kc * 16);
-        rstep_a = (unsigned)(32 * g.lda);
+        // K-contiguous tiles: load round it, thread tid fills slot it*NT + tid =
+        // (row it*NT/CPRK + tid/CPRK, physical chunk tid%CPRK), i.e. logical chunk
+        // (tid%CPRK) ^ swz(row) = (tid%CPRK) ^ ((tid/16)%CPRK), the same in every round
+        kc = (tid % C::CPRK) ^ ((tid >> 4) % C::CPRK);
+        loff_a = (unsigned)((tid / C::CPRK) * g.lda) + (unsigned)(kc * 16);
+        rstep_a = (unsigned)((C::NT / C::CPRK) * g.lda);
         if constexpr (BKN) {
             // B stored K x N: row k of the tile is 512 bytes = 8 granules of 64
-            // bytes; round it, thread tid fills slot it*256 + tid = (row it*8 +
+            // bytes; round it, thread tid fills slot it*NT + tid = (row it*NT/32 +
             // tid/32, physical 16-byte chunk tid%32), i.e. granule (tid%32)/4 ^
-            // (row % 8) = (tid%32)/4 ^ (tid/32) and chunk tid%4 within it
-            const int gran = ((tid & 31) >> 2) ^ (tid >> 5);
+            // (row % 8) = (tid%32)/4 ^ ((tid/32)%8) and chunk tid%4 within it
+            const int gran = ((tid & 31) >> 2) ^ ((tid >> 5) & 7);
             loff_b = (unsigned)((tid >> 5) * g.ldb) + (unsigned)(gran * 64 + (tid & 3) * 16);
-            rstep_b = (unsigned)(8 * g.ldb);
+            rstep_b = (unsigned)((C::NT / 32) * g.ldb);
         } else {
-            loff_b = (unsigned)((tid >> 3) * g.ldb) + (unsigned)(kc * 16);
-            rstep_b = (unsigned)(32 * g.ldb);
+            loff_b = (unsigned)((tid / C::CPRK) * g.ldb) + (unsigned)(kc * 16);
+            rstep_b = (unsigned)((C::NT / C::CPRK) * g.ldb);
         }
-        cx = (unsigned)((l32 >> 1) & 7);
+        cx = (unsigned)((l32 / C::RPL) % C::CPRK);
         ra = (unsigned)(C::AOFF + (wm * C::WM + l32) * C::ROWB);
         rb = (unsigned)(C::BOFF + (wn * C::WN + l32) * C::ROWB);
 #pragma unroll
@@ -362,22 +376,41 @@ struct Tile {
 
 #endif  // __HIP_DEVICE_COMPILE__
 
-template <int DT, bool BKN>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_kernel(GemmArgs g) {
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+template <int DT, bool BKN, int WAVES, int WAVES_N, int BK, int STAGES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
+void gemm_kernel(GemmArgs g) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    using C = Cfg;
+    using C = Cfg<WAVES, WAVES_N, BK, STAGES>;
     __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS];
-    Tile<DT, BKN> t;
+    Tile<DT, BKN, C> t;
     int tile_m, tile_n;
     map_tile(g, tile_m, tile_n);
     t.init(g, (unsigned)(size_t)(lds_bytes)lds, tile_m, tile_n);
     const int nk = (g.K + C::BK - 1) / C::BK;
-    if (nk > 0) t.issue(g, 0, 0);
+    // tiles 0 .. STAGES-2 in flight before the loop; step j waits for tile j
+    // (the loads of up to STAGES-2 later tiles may stay outstanding), then every
+    // wave has left step j-1, so tile j+STAGES-1 may refill that step's stage
+#pragma unroll
+    for (int p = 0; p < STAGES - 1; ++p)
+        if (p < nk) t.issue(g, p, p * C::STAGE);
     for (int j = 0; j < nk; ++j) {
-        wait_loads();
+        const int later = min(STAGES - 2, nk - 1 - j);   // tiles issued after tile j, still loading
+        if constexpr (STAGES >= 4) {
+            if (later >= 2) wait_vmcnt<2 * C::LOADS>();
+            else if (later == 1) wait_vmcnt<C::LOADS>();
+            else wait_vmcnt<0>();
+        } else if constexpr (STAGES == 3) {
+            if (later >= 1) wait_vmcnt<C::LOADS>();
+            else wait_vmcnt<0>();
+        } else {
+            wait_vmcnt<0>();
+        }
         __syncthreads();
-        if (j + 1 < nk) t.issue(g, j + 1, ((j + 1) & 1) * C::STAGE);
-        t.compute((j & 1) * C::STAGE);
+        if (j + STAGES - 1 < nk) t.issue(g, j + STAGES - 1, ((j + STAGES - 1) % STAGES) * C::STAGE);
+        t.compute((j % STAGES) * C::STAGE);
     }
     t.finish(g);
 #endif
@@ -405,6 +438,34 @@ int check_device() {
 
 bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
 
+// the launched configuration: waves per work-group, how many of them split n,
+// the k step and the number of LDS stages
+#ifndef ETA_GEMM_WAVES
+#define ETA_GEMM_WAVES 8
+#endif
+#ifndef ETA_GEMM_WAVES_N
+#define ETA_GEMM_WAVES_N 2
+#endif
+#ifndef ETA_GEMM_BK
+#define ETA_GEMM_BK 64
+#endif
+#ifndef ETA_GEMM_STAGES
+#define ETA_GEMM_STAGES 2
+#endif
+
+template <int WAVES, int WAVES_N, int BK, int STAGES>
+hipError_t launch(const GemmArgs& g, int dtype, bool bkn, hipStream_t s) {
+    const dim3 grid((unsigned)(g.tm * g.tn)), block(64 * WAVES);
+    if (dtype == ATTN_BF16) {
+        if (bkn) hipLaunchKernelGGL((gemm_kernel<ATTN_BF16, true, WAVES, WAVES_N, BK, STAGES>), grid, block, 0, s, g);
+        else hipLaunchKernelGGL((gemm_kernel<ATTN_BF16, false, WAVES, WAVES_N, BK, STAGES>), grid, block, 0, s, g);
+    } else {
+        if (bkn) hipLaunchKernelGGL((gemm_kernel<ATTN_F16, true, WAVES, WAVES_N, BK, STAGES>), grid, block, 0, s, g);
+        else hipLaunchKernelGGL((gemm_kernel<ATTN_F16, false, WAVES, WAVES_N, BK, STAGES>), grid, block, 0, s, g);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 extern "C" int gemm_bias_act(const void* a, long long lda, const void* b, long long ldb, int b_layout, const void* bias,
@@ -420,7 +481,7 @@ extern "C" int gemm_bias_act(const void* a, long long lda, const void* b, long l
         if (lda < K || ldb < (bkn ? N : K)) return ATTN_ERR_SHAPE;
         // 32-bit buffer offsets: one panel of A (and of B) must span < 2^31 bytes
         constexpr long long kSpan = 1LL << 31;
-        if (lda > kSpan / (2 * Cfg::BM) || ldb > kSpan / (2 * (bkn ? Cfg::BK : Cfg::BN))) return ATTN_ERR_SHAPE;
+        if (lda > kSpan / (2 * Shape::BM) || ldb > kSpan / (2 * (bkn ? Shape::BK : Shape::BN))) return ATTN_ERR_SHAPE;
         if (((uintptr_t)a | (uintptr_t)b) % 16 || lda % 8 || ldb % 8) return ATTN_ERR_ALIGN;
     }
     if (ldc > (1LL << 40)) return ATTN_ERR_SHAPE;
@@ -434,7 +495,7 @@ extern "C" int gemm_bias_act(const void* a, long long lda, const void* b, long l
         if (overlaps(c0, c1, a0, a1) || overlaps(c0, c1, b0, b1)) return ATTN_ERR_ALIAS;
     }
     if (bias && overlaps(c0, c1, (uintptr_t)bias, (uintptr_t)bias + (uintptr_t)N * 2)) return ATTN_ERR_ALIAS;
-    const long long tm = ((long long)M + Cfg::BM - 1) / Cfg::BM, tn = ((long long)N + Cfg::BN - 1) / Cfg::BN;
+    const long long tm = ((long long)M + Shape::BM - 1) / Shape::BM, tn = ((long long)N + Shape::BN - 1) / Shape::BN;
     if (tm * tn > 0x7fffffffLL) return ATTN_ERR_SHAPE;
     const int dev_status = check_device();
     if (dev_status != ATTN_OK) return dev_status;
@@ -454,14 +515,6 @@ extern "C" int gemm_bias_act(const void* a, long long lda, const void* b, long l
     g.tm = (int)tm;
     g.tn = (int)tn;
     g.c_vec = ((uintptr_t)c % 8 == 0) && (ldc % 4 == 0);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const dim3 grid((unsigned)(tm * tn)), block(Cfg::NT);
-    if (dtype == ATTN_BF16) {
-        if (bkn) hipLaunchKernelGGL((gemm_kernel<ATTN_BF16, true>), grid, block, 0, s, g);
-        else hipLaunchKernelGGL((gemm_kernel<ATTN_BF16, false>), grid, block, 0, s, g);
-    } else {
-        if (bkn) hipLaunchKernelGGL((gemm_kernel<ATTN_F16, true>), grid, block, 0, s, g);
-        else hipLaunchKernelGGL((gemm_kernel<ATTN_F16, false>), grid, block, 0, s, g);
-    }
-    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+    return launch<ETA_GEMM_WAVES, ETA_GEMM_WAVES_N, ETA_GEMM_BK, ETA_GEMM_STAGES>(g, dtype, bkn,
+                                                                                 static_cast<hipStream_t>(stream)) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
