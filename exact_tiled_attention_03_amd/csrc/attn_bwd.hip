@@ -474,24 +474,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     }
                 // P and dS; register i of block sb is query qt0 + 32 sb + 16 (i/8) + 8 hf + i%8,
                 // kept when it is < N and (causal) >= the key; its lse and D are
-                // read from the stage (rows 32 sb + 16 (i/8) + 8 hf + 0..7)
-                const bool edge = (CAUSAL && qt0 < kw0 + 31) || qt0 + C::BT > N;
-                u32x4_t pf[4], dsf[4];
+                // read from the stage (rows 32 sb + 16 (i/8) + 8 hf + 0..7).  The
+                // exponent arguments are formed first, masked (edge tiles only,
+                // one uniform branch) to -inf, then exponentiated.
+                float dr[4][8];
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
-                    float pv[8], dv8[8], lr[8], dr[8];
+                    float lr[8];
                     st.floats8(stg, 0, 16 * kk + 8 * st.hf, lr);
-                    st.floats8(stg, 1, 16 * kk + 8 * st.hf, dr);
+                    st.floats8(stg, 1, 16 * kk + 8 * st.hf, dr[kk]);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
                         const int sb = kk >> 1, reg = 8 * (kk & 1) + i;
-                        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][reg], a.c, -lr[i] * kLog2e));
-                        if (edge) {
-                            const int qrow = qt0 + 32 * sb + 16 * (reg >> 3) + 8 * st.hf + (reg & 7);
-                            if (qrow >= N || (CAUSAL && qrow < kj)) p = 0.f;
+                        s[sb][reg] = __builtin_fmaf(s[sb][reg], a.c, -lr[i] * kLog2e);
+                    }
+                }
+                if ((CAUSAL && qt0 < kw0 + 31) || qt0 + C::BT > N) {
+                    const int lim = (CAUSAL ? kj : 0) - (qt0 + 8 * st.hf);   // keep rows r with r >= lim
+                    const int top = N - (qt0 + 8 * st.hf);                     // and r < top
+#pragma unroll
+                    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                        for (int reg = 0; reg < 16; ++reg) {
+                            const int r = 32 * sb + 16 * (reg >> 3) + (reg & 7);
+                            if (r >= top || r < lim) s[sb][reg] = -__builtin_huge_valf();
                         }
+                }
+                u32x4_t pf[4], dsf[4];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    float pv[8], dv8[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int sb = kk >> 1, reg = 8 * (kk & 1) + i;
+                        const float p = __builtin_amdgcn_exp2f(s[sb][reg]);
                         pv[i] = p;
-                        dv8[i] = p * (dp[sb][reg] - dr[i]);
+                        dv8[i] = p * (dp[sb][reg] - dr[kk][i]);
                     }
                     pf[kk] = u32x4_t{E::pack2(pv[0], pv[1]), E::pack2(pv[2], pv[3]), E::pack2(pv[4], pv[5]), E::pack2(pv[6], pv[7])};
                     dsf[kk] = u32x4_t{E::pack2(dv8[0], dv8[1]), E::pack2(dv8[2], dv8[3]), E::pack2(dv8[4], dv8[5]),
