@@ -145,8 +145,9 @@ __device__ __forceinline__ int kperm(int m) {
 //    granule per 32 lanes: the granule index g of row r sits at g ^ vswz(r),
 //    vswz(r) = (r / RPB) % GPR with GPR granules per row.  It only moves whole
 //    granules, so rows 4 apart differ by a fixed offset for every lane.
-template <int D, int WAVES_> struct Cfg {
+template <int D, int WAVES_, int STAGES_ = 2> struct Cfg {
     static constexpr int WAVES = WAVES_;
+    static constexpr int STAGES = STAGES_;            // K/V tile stages in LDS
     static constexpr int NT = 64 * WAVES;             // threads per work-group
     static constexpr int BM = 32 * WAVES;             // queries per work-group (32 per wave)
     static constexpr int BN = 64;                     // keys per tile
@@ -161,15 +162,16 @@ template <int D, int WAVES_> struct Cfg {
     static constexpr int GPR = CPRP / 4;              // 64-byte granules per row
     static constexpr int TILEB = BN * ROWB;           // bytes of one K or V tile
     static constexpr int KOFF = 0;                    // K stage s at KOFF + s * TILEB
-    static constexpr int VOFF = 2 * TILEB;            // V stage s at VOFF + s * TILEB
-    static constexpr int LDS = 4 * TILEB;
+    static constexpr int VOFF = STAGES * TILEB;       // V stage s at VOFF + s * TILEB
+    static constexpr int LDS = 2 * STAGES * TILEB;
     static constexpr int IT = TILEB / (16 * NT);      // direct-load instructions per tile and thread
     static __device__ __forceinline__ int kswz(int r) { return (r / RPB) % CPRP; }
     static __device__ __forceinline__ int vswz(int r) { return (r / RPB) % GPR; }
     static_assert(D % 16 == 0 && CPR <= CPRP, "head dim");
     static_assert(IT >= 1 && TILEB % (16 * NT) == 0, "a tile is a whole number of load rounds");
     static_assert(DBLK <= GPR, "transpose reads of the padded head dim stay inside a row");
-    static_assert(VOFF + 2 * TILEB <= 65536, "LDS offsets fit the 16-bit immediate");
+    static_assert(STAGES == 3 || VOFF + 2 * TILEB <= 65536, "LDS offsets fit the 16-bit immediate");
+    static_assert(LDS <= 160 * 1024, "LDS");
 };
 
 typedef __fp16 lds_v4h_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
@@ -206,9 +208,9 @@ __device__ __forceinline__ void map_workgroup(const FwdArgs& a, int& bh, int& gr
 
 // State and arithmetic of one wave: 32 query rows (one per accumulator column;
 // the two lanes of a column each hold half of the keys of a tile).
-template <int D, int DT, bool CAUSAL, int WAVES, bool WIN>
+template <int D, int DT, bool CAUSAL, int WAVES, bool WIN, int STAGES = 2>
 struct Wave {
-    using C = Cfg<D, WAVES>;
+    using C = Cfg<D, WAVES, STAGES>;
     using E = Elem<DT>;
     static constexpr int SB = C::SB, KK = C::KK, KSTEPS = C::KSTEPS, DBLK = C::DBLK, CPR = C::CPR;
 
@@ -324,6 +326,26 @@ struct Wave {
                 s[sb] = E::mfma(lds_read16(ka[ks] + ST * C::TILEB + sb * 32 * C::ROWB), qf[ks], s[sb]);
     }
 
+    // K fragments of the tile in stage ST (the score MFMAs' A operands), read
+    // ahead of the step that uses them
+    template <int ST>
+    __device__ __forceinline__ void kread(u32x4_t (&kf)[KSTEPS][SB]) const {
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+            for (int sb = 0; sb < SB; ++sb) kf[ks][sb] = lds_read16(ka[ks] + ST * C::TILEB + sb * 32 * C::ROWB);
+    }
+
+    // S^T = K Q^T from K fragments already in registers
+    __device__ __forceinline__ void score_reg(const u32x4_t (&kf)[KSTEPS][SB], f32x16_t (&s)[SB]) const {
+#pragma unroll
+        for (int sb = 0; sb < SB; ++sb) s[sb] = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+            for (int sb = 0; sb < SB; ++sb) s[sb] = E::mfma(kf[ks][sb], qf[ks], s[sb]);
+    }
+
     // Mask tile j's scores where needed and update the reference max.  m is
     // raised only when a tile's max exceeds it by more than ETA_RESCALE_TH (log2
     // units), so p <= 2^TH and the O rescale is rare; m, l and O always refer to
@@ -420,15 +442,28 @@ struct Wave {
 #endif  // __HIP_DEVICE_COMPILE__
 
 // ---- the kernel: WAVES free-running waves per work-group ---------------------
+// The 8-wave schedule without a window runs a three-stage K/V ring: the
+// barrier of step j sits between its score MFMAs and its softmax.  It makes
+// tile j+1 visible (its loads were issued a step earlier) and frees the stage
+// of tile j-1 (every wave has finished that tile's P.V), which then receives
+// tile j+2.  Right after it the wave reads tile j+1's K fragments, so the next
+// step's score MFMAs start from registers with no barrier or LDS wait in front
+// of them.
+#ifndef ETA_FWD_RING
+#define ETA_FWD_RING 1
+#endif
+template <int WAVES, bool WIN> constexpr int fwd_stages() { return ETA_FWD_RING && WAVES == 8 && !WIN ? 3 : 2; }
+
 template <int D, int DT, bool CAUSAL, int WAVES, bool WIN>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
-    using C = Cfg<D, WAVES>;
+    constexpr int STAGES = fwd_stages<WAVES, WIN>();
+    using C = Cfg<D, WAVES, STAGES>;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    Wave<D, DT, CAUSAL, WAVES, WIN> w;
+    Wave<D, DT, CAUSAL, WAVES, WIN, STAGES> w;
     w.init(a, (unsigned)(size_t)(lds_bytes)smem, tid, wave);
 
     int bh, grp;
@@ -444,6 +479,50 @@ void attn_fwd_kernel(FwdArgs a) {
         const int kend = CAUSAL ? min(a.N, q0 + C::BM) : (win > 0 ? min(a.N, q0 + C::BM - 1 + win) : a.N);
         const int nt = (kend + C::BN - 1) / C::BN;
         const int jlo = win > 0 ? max(0, q0 - win + 1) / C::BN : 0;
+
+        if constexpr (STAGES == 3) {
+            if (item > 0) __syncthreads();                 // every wave has left the previous item's tiles
+            u32x4_t kf[C::KSTEPS][C::SB];
+            auto rstep = [&](auto stage_tag, int j) {
+                constexpr int ST = decltype(stage_tag)::value, ST1 = (ST + 1) % 3, ST2 = (ST + 2) % 3;
+                const bool act = w.active(j);
+                f32x16_t s[C::SB];
+                if (act) {
+                    __builtin_amdgcn_s_setprio(2);
+                    w.score_reg(kf, s);
+                    __builtin_amdgcn_s_setprio(0);
+                }
+                wait_loads();                               // this wave's share of tile j+1
+                __syncthreads();                            // tile j+1 visible, tile j-1's stage free
+                if (j + 2 < nt) {
+                    w.issue(false, j + 2, ST2);
+                    w.issue(true, j + 2, ST2);
+                }
+                if (j + 1 < nt && w.active(j + 1)) w.template kread<ST1>(kf);
+                if (act) {
+                    u32x4_t pf[C::KK];
+                    w.prepare(s, j);
+                    w.probs(s, pf);
+                    w.template pv<ST>(pf);
+                }
+            };
+            w.issue(false, jlo, 0);
+            w.issue(true, jlo, 0);
+            if (jlo + 1 < nt) {
+                w.issue(false, jlo + 1, 1);
+                w.issue(true, jlo + 1, 1);
+            }
+            wait_loads();
+            __syncthreads();
+            if (w.active(jlo)) w.template kread<0>(kf);
+            for (int j = jlo; j < nt; j += 3) {             // tile j in stage (j - jlo) % 3
+                rstep(std::integral_constant<int, 0>{}, j);
+                if (j + 1 < nt) rstep(std::integral_constant<int, 1>{}, j + 1);
+                if (j + 2 < nt) rstep(std::integral_constant<int, 2>{}, j + 2);
+            }
+            w.finish(a, bh);
+            continue;
+        }
 
         // one step: prefetch tile j+1 into the other stage, compute tile j, sync.
         // The wave raises its priority while it issues the score MFMAs, so the
