@@ -24,6 +24,10 @@ the backward; recomputing S and dP in the dQ kernel is not credited).
 matrix product with its fused bias + activation epilogue: TFLOP/s counting
 2*M*N*K, against the dense bf16/fp16 MFMA peak.
 
+Warm-up: W untimed steps (default 100), continued until at least 0.25 s of
+warm-up has passed so that the K timed steps see a settled GPU clock (a cold
+start measured ~10% slower); the JSON line's warmup_detail says what was run.
+
 Traffic calibration (run each under rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE):
     python bench.py --copy-calibration          # plain 256 MiB copy kernel, known bytes
     python bench.py --traffic-summary ATTN_FETCH ATTN_WRITE COPY_FETCH COPY_WRITE
@@ -141,6 +145,27 @@ def traffic_summary(attn_fetch, attn_write, copy_fetch, copy_write, workload, ca
     print(json.dumps({key: entry}))
 
 
+SETTLE_S = 0.25   # minimum untimed warm-up time: the GPU clock ramps up over the first ~100 ms of load
+
+
+def warm_up(call, steps: int) -> dict:
+    """Run `steps` untimed warm-up steps, then keep going until SETTLE_S seconds of
+    warm-up have passed, so that the timed steps see a settled clock.  Returns what
+    was done (reported in the JSON line)."""
+    import torch
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    extra = 0
+    while time.perf_counter() - t0 < SETTLE_S:
+        for _ in range(10):
+            call()
+        extra += 10
+        torch.cuda.synchronize()
+    return {"steps": steps, "extra_settle_steps": extra, "seconds": round(time.perf_counter() - t0, 3)}
+
+
 def kept_pairs(n: int, causal: int, window: int, rows=None) -> float:
     """Number of (query, key) pairs the mask keeps in one head (for the given query
     rows, default all): key j is kept for query i when j <= i (causal) and, with a
@@ -239,9 +264,7 @@ def bench_softmax(args, w):
     x = aw.make_rows(w.rows, w.cols, w.dtype, w.seed, w.sigma).to(dev)
     y = torch.empty_like(x)
     stream = torch.cuda.current_stream()
-    for _ in range(args.warmup):
-        eta.softmax_rows(x, y, stream=stream)
-    torch.cuda.synchronize()
+    warm = warm_up(lambda: eta.softmax_rows(x, y, stream=stream), args.warmup)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t_begin = torch.cuda.Event(enable_timing=True)
@@ -270,6 +293,7 @@ def bench_softmax(args, w):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_detail": warm,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -332,9 +356,7 @@ def bench_gemm(args, w):
     def call():
         eta.gemm_bias_act(a, b, bias, w.act, w.b_layout, c=c, stream=stream)
 
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
+    warm = warm_up(call, args.warmup)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t_begin = torch.cuda.Event(enable_timing=True)
@@ -362,6 +384,7 @@ def bench_gemm(args, w):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_detail": warm,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -401,9 +424,7 @@ def bench_backward(args, w, causal):
     def call():
         eta.attn_bwd(q, k, v, out, lse, do, dq, dk, dv, delta, causal=bool(causal), scale=w.scale, stream=stream)
 
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
+    warm = warm_up(call, args.warmup)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t_begin = torch.cuda.Event(enable_timing=True)
@@ -430,6 +451,7 @@ def bench_backward(args, w, causal):
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_detail": warm,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -485,7 +507,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=None, help="workload name (default: the headline workload)")
     ap.add_argument("--causal", type=int, default=None)
     ap.add_argument("--window", type=int, default=0,
@@ -541,9 +563,8 @@ def main():
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
-    for _ in range(args.warmup):
-        eta.attn_fwd(q, k, v, out, lse, causal, w.scale, stream=stream, window=args.window)
-    torch.cuda.synchronize()
+    warm = warm_up(lambda: eta.attn_fwd(q, k, v, out, lse, causal, w.scale, stream=stream, window=args.window),
+                   args.warmup)
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -573,6 +594,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_detail": warm,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
