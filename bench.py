@@ -20,6 +20,11 @@ once and y written once, against the 8 TB/s HBM roofline.
 workload, crediting 2.5x the forward's FLOPs (the five N x N x d products of
 the backward; recomputing S and dP in the dQ kernel is not credited).
 
+--merge G times attn_lse_merge combining G key shards of the attention workload's
+shape (o_parts [G, B, H, N, d], lse_parts [G, B, H, N]): effective bandwidth in
+GB/s counting every part read once and the result written once, against the
+8 TB/s HBM roofline.
+
 --workload gemm_qkv_m8192_n12288_k4096_bf16 (or another gemm workload) times the
 matrix product with its fused bias + activation epilogue: TFLOP/s counting
 2*M*N*K, against the dense bf16/fp16 MFMA peak.
@@ -50,11 +55,15 @@ METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak, causal N=4096 d=128"
 METRIC_BWD = "attention bwd TFLOP/s (2.5x the forward's 4*B*H*N^2*d, halved for causal) and % of bf16 MFMA peak"
 METRIC_WINDOW = "sliding-window attention fwd TFLOP/s (4*d per kept query-key pair) and % of bf16 MFMA peak"
 METRIC_SOFTMAX = "row softmax effective bandwidth GB/s (x read once + y written once)"
+METRIC_MERGE = "key-shard merge effective bandwidth GB/s (G partial O and lse read once, merged O and lse written once)"
 MFMA_PEAK_TFLOPS = 2516.6      # dense fp16/bf16: 256 CU x 4096 FLOP/clk x 2.4 GHz (the 2.5 PFLOP/s figure)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 KERNEL_SOURCE = os.path.join(ROOT, "exact_tiled_attention_03_amd", "csrc", "attn_fwd.hip")
 SOFTMAX_SOURCE = os.path.join(ROOT, "exact_tiled_attention_03_amd", "csrc", "softmax_rows.hip")
 GEMM_SOURCE = os.path.join(ROOT, "exact_tiled_attention_03_amd", "csrc", "gemm.hip")
+BWD_SOURCE = os.path.join(ROOT, "exact_tiled_attention_03_amd", "csrc", "attn_bwd.hip")
+MERGE_SOURCE = os.path.join(ROOT, "exact_tiled_attention_03_amd", "csrc", "lse_merge.hip")
+BWD_KERNELS = ("attn_bwd_delta_kernel", "attn_bwd_dq_kernel", "attn_bwd_dkdv_kernel")
 METRIC_GEMM = "GEMM + bias + activation TFLOP/s (2*M*N*K) and % of bf16 MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -78,7 +87,7 @@ def traffic_key(workload: str, causal, window: int = 0) -> str:
     return f"{workload}-causal{causal}" + (f"-window{window}" if window > 0 else "")
 
 
-def measured_traffic(workload: str, causal: int, window: int = 0, source: str = KERNEL_SOURCE):
+def measured_traffic(workload: str, causal: int, window: int = 0, source: str = KERNEL_SOURCE, key=None):
     """HBM bytes per launch from the committed rocprofv3 counter runs, or None when
     absent or when the kernel source changed since they were taken."""
     try:
@@ -86,7 +95,7 @@ def measured_traffic(workload: str, causal: int, window: int = 0, source: str = 
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    entry = t.get(traffic_key(workload, causal, window))
+    entry = t.get(key or traffic_key(workload, causal, window))
     if not entry or entry.get("source_sha256_16") != source_hash(source):
         return None
     return entry.get("bytes_per_launch")
@@ -120,25 +129,32 @@ def _pmc_kib_per_dispatch(directory: str, counter: str, kernel_substr: str) -> f
 
 
 def traffic_summary(attn_fetch, attn_write, copy_fetch, copy_write, workload, causal, window=0,
-                    kernel_substr="attn_fwd_kernel", source=KERNEL_SOURCE):
+                    kernel_substr="attn_fwd_kernel", source=KERNEL_SOURCE, key=None):
     """HBM bytes per kernel launch: FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by
-    the ratio of known bytes to what the same counter reads for the plain copy kernel."""
+    the ratio of known bytes to what the same counter reads for the plain copy kernel.
+    kernel_substr may be a tuple: the entry is then the sum over those kernels (the
+    kernels of one entry-point call)."""
     f_copy = _pmc_kib_per_dispatch(copy_fetch, "FETCH_SIZE", "elementwise") * 1024
     w_copy = _pmc_kib_per_dispatch(copy_write, "WRITE_SIZE", "elementwise") * 1024
-    f_attn = _pmc_kib_per_dispatch(attn_fetch, "FETCH_SIZE", kernel_substr) * 1024
-    w_attn = _pmc_kib_per_dispatch(attn_write, "WRITE_SIZE", kernel_substr) * 1024
+    names = kernel_substr if isinstance(kernel_substr, tuple) else (kernel_substr,)
+    f_attn = sum(_pmc_kib_per_dispatch(attn_fetch, "FETCH_SIZE", n) for n in names) * 1024
+    w_attn = sum(_pmc_kib_per_dispatch(attn_write, "WRITE_SIZE", n) for n in names) * 1024
     f_scale, w_scale = COPY_BYTES / f_copy, COPY_BYTES / w_copy
     entry = {"bytes_per_launch": round(f_attn * f_scale + w_attn * w_scale),
              "read_bytes": round(f_attn * f_scale), "written_bytes": round(w_attn * w_scale),
              "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
              "raw_fetch_kib": f_attn / 1024, "raw_write_kib": w_attn / 1024,
              "source_sha256_16": source_hash(source)}
+    if len(names) > 1:
+        entry["per_kernel"] = {n: {"read_bytes": round(_pmc_kib_per_dispatch(attn_fetch, "FETCH_SIZE", n) * 1024 * f_scale),
+                                   "written_bytes": round(_pmc_kib_per_dispatch(attn_write, "WRITE_SIZE", n) * 1024 * w_scale)}
+                               for n in names}
     try:
         with open(TRAFFIC_FILE) as f:
             table = json.load(f)
     except (OSError, ValueError):
         table = {}
-    key = traffic_key(workload, causal, window)
+    key = key or traffic_key(workload, causal, window)
     table[key] = entry
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(table, f, indent=1, sort_keys=True)
@@ -464,13 +480,93 @@ def bench_backward(args, w, causal):
                    "launch_ms_min": round(min(per_launch), 5),
                    "note": "one step = the delta, dQ and dK/dV kernels of one attn_bwd call"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "attn_bwd_delta_kernel + attn_bwd_dq_kernel + attn_bwd_dkdv_kernel",
+                     "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(w.name, causal, 0, BWD_SOURCE, key=f"{w.name}-causal{causal}-backward"),
+                     "kernel": " + ".join(BWD_KERNELS),
                      "algorithmic_flops_per_launch": flops},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = backward_cpu_baseline(w, causal, q, k, v, do, dq, dk, dv, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def bench_merge(args, w, G):
+    """One step = one attn_lse_merge call over G shards of the workload's rows."""
+    import numpy as np
+    import torch
+    import attn_workloads as aw
+    import exact_tiled_attention_03_amd as eta
+    from oracle import backward as ob
+
+    dev = torch.device("cuda:0")
+    # seeded synthetic shard results of the workload's shape: the merge's cost does not
+    # depend on the values (o_parts iid N(0, 1) in the workload's type, lse_parts N(5, 2^2))
+    rng = np.random.default_rng(w.seed + 900)
+    shape = (G, w.B, w.H, w.N, w.d)
+    o_parts = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32)).to(aw.DTYPES[w.dtype]).to(dev)
+    l_parts = torch.from_numpy(5.0 + 2.0 * rng.standard_normal(shape[:4], dtype=np.float32)).to(dev)
+    o = torch.empty(shape[1:], dtype=o_parts.dtype, device=dev)
+    lse = torch.empty(shape[1:4], dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        eta.attn_lse_merge(o_parts, l_parts, o, lse, stream=stream)
+
+    warm = warm_up(call, args.warmup)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+    per_launch = [x.elapsed_time(y) for x, y in zip(starts, ends)]
+    ms_per_step = total_ms / args.steps
+    launch_ms = statistics.mean(per_launch)
+    rows = w.B * w.H * w.N
+    nbytes = G * rows * (w.d * 2 + 4) + rows * (w.d * 2 + 4)
+    value = nbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC_MERGE, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "warmup_detail": warm, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded shard results: O_g iid N(0,1), lse_g iid N(5,4))",
+        "config": {"workload": f"{w.name}-merge{G}", "G": G, "rows": rows, "d": w.d,
+                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                   "launch_ms_median": round(statistics.median(per_launch), 5)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(w.name, None, 0, MERGE_SOURCE, key=f"{w.name}-merge{G}"),
+                     "kernel": "lse_merge_kernel",
+                     "algorithmic_bytes_per_launch": nbytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        cores = len(os.sched_getaffinity(0))
+        sl = slice(0, 4)   # 4 heads of batch 0
+        op = o_parts[:, 0, sl].cpu().double().numpy()
+        lp = l_parts[:, 0, sl].cpu().double().numpy()
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0):
+            ro, rl = ob.lse_merge(op, lp)
+            reps += 1
+        dt = time.perf_counter() - t0
+        err = float(np.abs(o[0, sl].cpu().double().numpy() - ro).max())
+        sample_rows = 4 * w.N
+        line["cpu_baseline"] = {"value": reps * (G + 1) * sample_rows * (w.d * 2 + 4) / dt / 1e9, "unit": "GB/s",
+                                "cores": 1, "kind": "oracle",
+                                "sample": f"{sample_rows} of {rows} rows (4 heads), {reps} repetitions",
+                                "seconds": round(dt, 3), "host_cpus": cores,
+                                "parity_of_timed_output": {"max_abs": err}}
     print(json.dumps(line), flush=True)
 
 
@@ -513,6 +609,7 @@ def main():
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window W >= 1 (attn_fwd_window); FLOPs then count kept pairs x 4d")
     ap.add_argument("--backward", action="store_true", help="time attn_bwd on the attention workload")
+    ap.add_argument("--merge", type=int, default=0, help="time attn_lse_merge over this many key shards")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -528,8 +625,15 @@ def main():
             traffic_summary(*args.traffic_summary, args.workload, None, 0, "gemm_kernel", GEMM_SOURCE)
             return
         w = aw.by_name(args.workload) if args.workload else aw.WORKLOADS[aw.HEADLINE]
-        traffic_summary(*args.traffic_summary, w.name, w.causal_modes[0] if args.causal is None else args.causal,
-                        args.window)
+        causal = w.causal_modes[0] if args.causal is None else args.causal
+        if args.backward:
+            traffic_summary(*args.traffic_summary, w.name, causal, 0, BWD_KERNELS, BWD_SOURCE,
+                            key=f"{w.name}-causal{causal}-backward")
+        elif args.merge > 0:
+            traffic_summary(*args.traffic_summary, w.name, None, 0, "lse_merge_kernel", MERGE_SOURCE,
+                            key=f"{w.name}-merge{args.merge}")
+        else:
+            traffic_summary(*args.traffic_summary, w.name, causal, args.window)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -556,6 +660,9 @@ def main():
     causal = w.causal_modes[0] if args.causal is None else args.causal
     if args.backward:
         bench_backward(args, w, causal)
+        return
+    if args.merge > 0:
+        bench_merge(args, w, args.merge)
         return
     dev = torch.device("cuda:0")
     q, k, v = (t.to(dev) for t in aw.workload_inputs(w))

@@ -3,9 +3,10 @@
 //
 // From the definition of lse (natural log of a row's softmax denominator): the
 // shards' (O_g, lse_g) combine as lse = ln sum_g exp(lse_g) and
-// O = sum_g exp(lse_g - lse) O_g.  Evaluated as m = max_g lse_g,
-// w_g = exp2((lse_g - m) log2 e), O = (sum_g w_g O_g) / sum_g w_g,
-// lse = m + ln sum_g w_g, all in fp32; a shard with lse_g = -inf has w_g = 0.
+// O = sum_g exp(lse_g - lse) O_g.  Evaluated with m = max_g lse_g (kept as a
+// running max, partial sums rescaled when it grows), w_g = exp2((lse_g - m)
+// log2 e), O = (sum_g w_g O_g) / sum_g w_g, lse = m + ln sum_g w_g, all in
+// fp32; a shard with lse_g = -inf has w_g = 0.
 //
 // gfx950 mapping: HBM-bound; 16 lanes own a row (one 16-byte chunk of 8
 // values each, d <= 128), so one wave merges 4 rows and every load of a shard
@@ -17,6 +18,15 @@
 #include <cstring>
 
 #include "attn_bwd.h"
+
+// Shards whose loads are issued together, and whether the parts (read once) and
+// the result (written once) bypass the caches.
+#ifndef ETA_MERGE_UNROLL
+#define ETA_MERGE_UNROLL 8
+#endif
+#ifndef ETA_MERGE_STREAM
+#define ETA_MERGE_STREAM 1
+#endif
 
 namespace {
 
@@ -63,36 +73,57 @@ struct MergeArgs {
     int G, CPR;
 };
 
+// One pass over the shards, four at a time (their loads in flight together),
+// with a running max m: when a shard's lse exceeds m, the partial sums are
+// first multiplied by exp(m_old - m_new), as in the online softmax.
 template <int DT>
 __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using T = Ty<DT>;
+    constexpr int U = ETA_MERGE_UNROLL;
     const int sub = threadIdx.x & 15;
+    const bool own = sub < a.CPR;
     const long long stride = (long long)gridDim.x * 16;
     for (long long r = ((long long)blockIdx.x * 256 + threadIdx.x) >> 4; r < a.R; r += stride) {
-        float m = kNegInf;
-        for (int g = 0; g < a.G; ++g) m = fmaxf(m, a.lse_parts[(long long)g * a.R + r]);
+        float m = kNegInf, tot = 0.f;
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        float tot = 0.f;
-        if (m > kNegInf) {
-            for (int g = 0; g < a.G; ++g) {
-                const float w = __builtin_amdgcn_exp2f((a.lse_parts[(long long)g * a.R + r] - m) * kLog2e);
-                tot += w;
-                if (sub < a.CPR) {
-                    const u32x4_t v = a.o_parts[((long long)g * a.R + r) * a.CPR + sub];
+        for (int g0 = 0; g0 < a.G; g0 += U) {
+            float lg[U];
+            u32x4_t v[U];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const unsigned u = v[i];
-                        acc[2 * i] = __builtin_fmaf(w, T::lo(u), acc[2 * i]);
-                        acc[2 * i + 1] = __builtin_fmaf(w, T::hi(u), acc[2 * i + 1]);
-                    }
+            for (int u = 0; u < U; ++u) {
+                const int g = g0 + u;
+                lg[u] = g < a.G ? a.lse_parts[(long long)g * a.R + r] : kNegInf;
+                const u32x4_t* src = a.o_parts + ((long long)g * a.R + r) * a.CPR + sub;
+                v[u] = u32x4_t{0, 0, 0, 0};
+                if (g < a.G && own) v[u] = ETA_MERGE_STREAM ? __builtin_nontemporal_load(src) : *src;
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (lg[u] > m) {                                   // -inf never exceeds m
+                    const float sc = __builtin_amdgcn_exp2f((m - lg[u]) * kLog2e);   // 0 while m is -inf
+                    tot *= sc;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[i] *= sc;
+                    m = lg[u];
+                }
+                const float w = lg[u] > kNegInf ? __builtin_amdgcn_exp2f((lg[u] - m) * kLog2e) : 0.f;
+                tot += w;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const unsigned x = v[u][i];
+                    acc[2 * i] = __builtin_fmaf(w, T::lo(x), acc[2 * i]);
+                    acc[2 * i + 1] = __builtin_fmaf(w, T::hi(x), acc[2 * i + 1]);
                 }
             }
         }
         const float inv = tot > 0.f ? 1.0f / tot : 0.f;
-        if (sub < a.CPR)
-            a.o[r * a.CPR + sub] = u32x4_t{T::pack2(acc[0] * inv, acc[1] * inv), T::pack2(acc[2] * inv, acc[3] * inv),
-                                           T::pack2(acc[4] * inv, acc[5] * inv), T::pack2(acc[6] * inv, acc[7] * inv)};
+        const u32x4_t res{T::pack2(acc[0] * inv, acc[1] * inv), T::pack2(acc[2] * inv, acc[3] * inv),
+                          T::pack2(acc[4] * inv, acc[5] * inv), T::pack2(acc[6] * inv, acc[7] * inv)};
+        if (own) {
+            if (ETA_MERGE_STREAM) __builtin_nontemporal_store(res, a.o + r * a.CPR + sub);
+            else a.o[r * a.CPR + sub] = res;
+        }
         if (sub == 0) a.lse[r] = m > kNegInf ? m + __builtin_amdgcn_logf(tot) * kLn2 : kNegInf;
     }
 #endif
