@@ -37,6 +37,7 @@
 #include <cstring>
 
 #include "attn_bwd.h"
+#include "lds_load.h"
 
 namespace {
 
@@ -213,15 +214,11 @@ struct Streams {
     // this wave's share of rows t0 .. t0+63 of `src` (rows past `rows` read as zero) into tile `which`
     __device__ __forceinline__ void issue(const unsigned char* src, int rows, int t0, int stage, int which) const {
         const int bytes = max(0, (rows - t0) * D * 2);
-        const __amdgpu_buffer_rsrc_t r =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(src + (size_t)t0 * D * 2), 0, bytes, 0x00020000);
+        const eta_desc_t desc = buffer_desc(src + (size_t)t0 * D * 2, bytes);
         const unsigned region = lds0 + stage * C::STAGE + (which ? C::YOFF : C::XOFF);
 #pragma unroll
-        for (int it = 0; it < C::IT; ++it) {
-            const unsigned dst = region + (unsigned)((it * C::WAVES + wave) * 64 * 16);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_bytes)(size_t)dst, 16,
-                                                     lo_off[it], 0, 0, 0);
-        }
+        for (int it = 0; it < C::IT; ++it)
+            load_lds16(desc, lo_off[it], 0, region + (unsigned)((it * C::WAVES + wave) * 64 * 16));
     }
 
     // BT consecutive floats src[t0 ..] (zero past `rows`) into float row `which` of
@@ -229,10 +226,7 @@ struct Streams {
     __device__ __forceinline__ void issue_floats(const float* src, int rows, int t0, int stage, int which) const {
         if (wave != 0) return;
         const int bytes = max(0, (rows - t0) * 4);
-        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)(src + t0), 0, bytes, 0x00020000);
-        const unsigned dst = lds0 + stage * C::STAGE + C::ROFF + which * C::BT * 4;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_bytes)(size_t)dst, 4,
-                                                 (unsigned)(lane * 4), 0, 0, 0);
+        load_lds4(buffer_desc(src + t0, bytes), (unsigned)(lane * 4), lds0 + stage * C::STAGE + C::ROFF + which * C::BT * 4);
     }
 
     // 8 consecutive floats of float row `which` starting at row r0 (a multiple of 8)

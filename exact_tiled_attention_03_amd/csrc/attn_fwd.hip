@@ -47,6 +47,7 @@
 #include <type_traits>
 
 #include "attn.h"
+#include "lds_load.h"
 
 namespace {
 
@@ -197,9 +198,8 @@ __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)"
 // Work-group id -> (head, group): ids are dealt round-robin over the 8 XCDs,
 // so XCD x runs ids x, x+8, ...; the remap gives each XCD a contiguous range
 // of (head, group) indices.
-__device__ __forceinline__ void map_workgroup(const FwdArgs& a, int& bh, int& grp) {
+__device__ __forceinline__ void map_workgroup(const FwdArgs& a, int L, int& bh, int& grp) {
     const int T = a.ngroups * a.BH;
-    const int L = blockIdx.x;
     const int xcd = L & 7;
     const int vidx = xcd * (T >> 3) + min(xcd, T & 7) + (L >> 3);
     bh = vidx / a.ngroups;
@@ -290,14 +290,11 @@ struct Wave {
         const int kt0 = j * C::BN;
         const int bytes = (N - kt0) * D * 2;            // rows kt0 .. N-1 are in range
         const unsigned char* base = (is_v ? vbase : kbase) + (size_t)kt0 * D * 2;
-        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, 0x00020000);
+        const eta_desc_t desc = buffer_desc(base, bytes);
         const unsigned region = lds0 + (is_v ? C::VOFF : C::KOFF) + stage * C::TILEB;
 #pragma unroll
-        for (int it = 0; it < C::IT; ++it) {
-            const unsigned dst = region + (unsigned)(slot_base(it) * 16);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_bytes)(size_t)dst, 16,
-                                                     is_v ? vvo[it] : kvo[it], 0, 0, 0);
-        }
+        for (int it = 0; it < C::IT; ++it)
+            load_lds16(desc, is_v ? vvo[it] : kvo[it], 0, region + (unsigned)(slot_base(it) * 16));
     }
 
     // first slot of load round `it` for this wave
@@ -368,11 +365,12 @@ struct Wave {
                     if (key > hi || (WIN && key < lo)) s[sb][i] = kNegInf;
                 }
         }
-        float mx = kNegInf;
+        float mc[4] = {kNegInf, kNegInf, kNegInf, kNegInf};   // four independent chains
 #pragma unroll
         for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[sb][i]);
+            for (int i = 0; i < 16; ++i) mc[i & 3] = fmaxf(mc[i & 3], s[sb][i]);
+        const float mx = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
         const float mt = pair_max(mx) * c;           // c > 0, so -inf stays -inf
         const bool grow = mt > m + ETA_RESCALE_TH;
         if (__any(grow)) {
@@ -417,6 +415,53 @@ struct Wave {
             }
     }
 
+    // The matrix half of a step: O^T += V^T P^T for the tile in V stage ST and
+    // S^T = K Q^T for the tile in K stage ST1, in rounds of up to two MFMAs of
+    // each.  The LDS operands of round r+PD are read before round r's MFMAs
+    // (scheduling fences keep the compiler from sinking the reads next to
+    // their MFMAs), so PD+1 rounds of operands are live at a time.
+#ifndef ETA_FWD_PD
+#define ETA_FWD_PD 1
+#endif
+    template <int ST, int ST1>
+    __device__ __forceinline__ void pv_score(const u32x4_t (&pf)[KK], f32x16_t (&s)[SB]) {
+        constexpr int NPV = KK * DBLK, NSC = KSTEPS * SB;
+        constexpr int R = ((NPV > NSC ? NPV : NSC) + 1) / 2;
+        constexpr int PD = ETA_FWD_PD < R ? ETA_FWD_PD : R - 1, NB = PD + 1;
+        u32x4_t vo[NB][2], ko[NB][2];
+        auto rd = [&](int r) {
+            const int b = r % NB;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int pi = 2 * r + i;
+                if (pi < NPV) {
+                    const int kk = pi / DBLK, db = pi % DBLK;
+                    const u32x2_t lo = lds_read_tr(va[db] + ST * C::TILEB + 16 * kk * C::ROWB);
+                    const u32x2_t hi = lds_read_tr(va[db] + ST * C::TILEB + (16 * kk + 4) * C::ROWB);
+                    vo[b][i] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+                }
+                if (pi < NSC) ko[b][i] = lds_read16(ka[pi / SB] + ST1 * C::TILEB + (pi % SB) * 32 * C::ROWB);
+            }
+        };
+#pragma unroll
+        for (int sb = 0; sb < SB; ++sb) s[sb] = f32x16_t{};
+#pragma unroll
+        for (int r = 0; r < PD; ++r) rd(r);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (r + PD < R) rd(r + PD);
+            __builtin_amdgcn_sched_barrier(0);
+            const int b = r % NB;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int pi = 2 * r + i;
+                if (pi < NPV) o[pi % DBLK] = E::mfma(vo[b][i], pf[pi / DBLK], o[pi % DBLK]);
+                if (pi < NSC) s[pi % SB] = E::mfma(ko[b][i], qf[pi / SB], s[pi % SB]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
     // O = acc / l rounded to the input type; lse = ln2 * (m + log2 l)
     __device__ __forceinline__ void finish(const FwdArgs& a, int bh) {
         if (qw0 >= N) return;
@@ -452,7 +497,14 @@ struct Wave {
 #ifndef ETA_FWD_RING
 #define ETA_FWD_RING 1
 #endif
-template <int WAVES, bool WIN> constexpr int fwd_stages() { return ETA_FWD_RING && WAVES == 8 && !WIN ? 3 : 2; }
+// The 8-wave schedule with two wave groups in alternation (see the kernel).
+#ifndef ETA_FWD_PING
+#define ETA_FWD_PING 1
+#endif
+template <int WAVES, bool WIN> constexpr bool fwd_ping() { return ETA_FWD_PING && WAVES == 8; }
+template <int WAVES, bool WIN> constexpr int fwd_stages() {
+    return fwd_ping<WAVES, WIN>() || (ETA_FWD_RING && WAVES == 8 && !WIN) ? 3 : 2;
+}
 
 template <int D, int DT, bool CAUSAL, int WAVES, bool WIN>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -466,10 +518,16 @@ void attn_fwd_kernel(FwdArgs a) {
     Wave<D, DT, CAUSAL, WAVES, WIN, STAGES> w;
     w.init(a, (unsigned)(size_t)(lds_bytes)smem, tid, wave);
 
+    // Work units (a query tile, or a causal pair of them) blockIdx.x,
+    // blockIdx.x + gridDim.x, ...: the grid is either one work-group per unit
+    // or, for the 8-wave kernel, a multiple of 8 work-groups that stay resident
+    // (a unit keeps its XCD since gridDim.x % 8 == 0).
+    bool first = true;
+    for (int unit = blockIdx.x; unit < a.ngroups * a.BH; unit += gridDim.x) {
     int bh, grp;
-    map_workgroup(a, bh, grp);
+    map_workgroup(a, unit, bh, grp);
     const int nitems = CAUSAL && grp != a.nqt - 1 - grp ? 2 : 1;
-    for (int item = 0; item < nitems; ++item) {
+    for (int item = 0; item < nitems; ++item, first = false) {
         const int qt = CAUSAL ? (item == 0 ? a.nqt - 1 - grp : grp) : grp;
         const int q0 = qt * C::BM;
         w.begin(a, bh, q0 + 32 * wave);
@@ -480,8 +538,83 @@ void attn_fwd_kernel(FwdArgs a) {
         const int nt = (kend + C::BN - 1) / C::BN;
         const int jlo = win > 0 ? max(0, q0 - win + 1) / C::BN : 0;
 
-        if constexpr (STAGES == 3) {
-            if (item > 0) __syncthreads();                 // every wave has left the previous item's tiles
+        if constexpr (fwd_ping<WAVES, WIN>()) {
+            // Two groups of four waves, one wave of each on every SIMD.  Every
+            // wave runs the same sequence per key tile u (u = 0 .. T-1 from jlo):
+            //     Y(u)  barrier  X(u)  barrier
+            // with Y(u) = the softmax half (mask, max, rescale, exponentials of
+            // tile u's scores into P) and X(u) = the matrix half (O^T += V^T P^T
+            // of tile u, then S^T = K Q^T of tile u+1).  Group 1 passes one
+            // extra barrier before its first Y and group 0 one after its last
+            // X, so between two barriers one wave of a SIMD issues MFMAs while
+            // the other works through its exponentials:
+            //     slot 2u+1: group 0 X(u),   group 1 Y(u)
+            //     slot 2u+2: group 0 Y(u+1), group 1 X(u)
+            // K/V tile u lives in LDS stage u % 3.  Tile u+2 is issued at the
+            // start of slot 2u+1 into the stage of tile u-1, whose V was last
+            // read in slot 2u, and every wave waits for its share at the end of
+            // slot 2u+2, before that tile's K is first read in slot 2u+3.
+            if (!first) __syncthreads();                   // every wave has left the previous item's tiles
+            const bool g0 = wave < 4;                      // wave-uniform
+            const int T = nt - jlo;
+            f32x16_t s[C::SB];                             // scores of the tile whose softmax is next
+            u32x4_t pf[C::KK];                             // P of the tile whose P.V is next
+            // One code path for the matrix half keeps register use low: a wave
+            // with no P.V for tile u multiplies a zero P, and a score computed
+            // past the wave's last tile is not used.
+            auto X = [&](auto stage_tag, int u) {
+                constexpr int ST = decltype(stage_tag)::value, ST1 = (ST + 1) % 3;
+                const bool do_pv = w.active(jlo + u), do_s = u + 1 < T && w.active(jlo + u + 1);
+                if (do_pv || do_s) {
+                    if (!do_pv) {
+#pragma unroll
+                        for (int kk = 0; kk < C::KK; ++kk) pf[kk] = u32x4_t{0, 0, 0, 0};
+                    }
+                    __builtin_amdgcn_s_setprio(2);
+                    w.template pv_score<ST, ST1>(pf, s);
+                    __builtin_amdgcn_s_setprio(0);
+                }
+            };
+            auto issue_tile = [&](auto stage_tag, int u) {
+                constexpr int ST2 = (decltype(stage_tag)::value + 2) % 3;
+                if (u + 2 < T) {
+                    w.issue(false, jlo + u + 2, ST2);
+                    w.issue(true, jlo + u + 2, ST2);
+                }
+            };
+            auto tile = [&](auto stage_tag, int u) {
+                if (!g0) issue_tile(stage_tag, u);          // slot 2u+1 starts (group 1)
+                if (w.active(jlo + u)) {
+                    w.prepare(s, jlo + u);
+                    w.probs(s, pf);
+                }
+                if (g0) wait_loads();                       // slot 2u ends (group 0): tile u+1 landed
+                __syncthreads();
+                if (g0) issue_tile(stage_tag, u);           // slot 2u+1 starts (group 0)
+                X(stage_tag, u);
+                if (!g0) wait_loads();                      // slot 2u+2 ends (group 1): tile u+2 landed
+                __syncthreads();
+            };
+            w.issue(false, jlo, 0);
+            w.issue(true, jlo, 0);
+            if (T > 1) {
+                w.issue(false, jlo + 1, 1);
+                w.issue(true, jlo + 1, 1);
+            }
+            wait_loads();
+            __syncthreads();
+            if (w.active(jlo)) w.template score<0>(s);
+            if (!g0) __syncthreads();
+            for (int u = 0; u < T; u += 3) {
+                tile(std::integral_constant<int, 0>{}, u);
+                if (u + 1 < T) tile(std::integral_constant<int, 1>{}, u + 1);
+                if (u + 2 < T) tile(std::integral_constant<int, 2>{}, u + 2);
+            }
+            if (g0) __syncthreads();
+            w.finish(a, bh);
+            continue;
+        } else if constexpr (STAGES == 3) {
+            if (!first) __syncthreads();                   // every wave has left the previous item's tiles
             u32x4_t kf[C::KSTEPS][C::SB];
             auto rstep = [&](auto stage_tag, int j) {
                 constexpr int ST = decltype(stage_tag)::value, ST1 = (ST + 1) % 3, ST2 = (ST + 2) % 3;
@@ -557,6 +690,7 @@ void attn_fwd_kernel(FwdArgs a) {
         }
         w.finish(a, bh);
     }
+    }
 #endif
 }
 
@@ -575,50 +709,71 @@ bool use_wide(long long bh, long long N, int causal) {
     return (causal ? (nqt + 1) / 2 : nqt) * bh >= kWideMinGroups;
 }
 
+// Resident work-groups for the 8-wave schedule: one per CU (its LDS stages
+// leave room for no second one), each looping over work units, so that the
+// grid runs as one round instead of several.
+#ifndef ETA_FWD_PERSIST
+#define ETA_FWD_PERSIST 1
+#endif
+
 template <int D, int DT, bool CAUSAL, int WAVES, bool WIN>
-hipError_t launch_waves(FwdArgs a, hipStream_t stream) {
+hipError_t launch_waves(FwdArgs a, hipStream_t stream, int cus) {
     constexpr int BM = Cfg<D, WAVES>::BM;
     const long long nqt = ((long long)a.N + BM - 1) / BM;
     a.nqt = (int)nqt;
     a.ngroups = CAUSAL ? (int)((nqt + 1) / 2) : (int)nqt;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, CAUSAL, WAVES, WIN>), dim3((unsigned)a.ngroups * (unsigned)a.BH),
-                       dim3(64 * WAVES), 0, stream, a);
+    const unsigned units = (unsigned)a.ngroups * (unsigned)a.BH;
+    unsigned grid = units;
+    if (ETA_FWD_PERSIST && fwd_ping<WAVES, WIN>() && cus >= 8 && units > (unsigned)cus) grid = (unsigned)cus & ~7u;
+    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, CAUSAL, WAVES, WIN>), dim3(grid), dim3(64 * WAVES), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int D, int DT, bool CAUSAL>
-hipError_t launch(FwdArgs a, hipStream_t stream) {
+hipError_t launch(FwdArgs a, hipStream_t stream, int cus) {
     const bool wide = use_wide(a.BH, a.N, CAUSAL);
     if (a.window > 0)
-        return wide ? launch_waves<D, DT, CAUSAL, 8, true>(a, stream) : launch_waves<D, DT, CAUSAL, 4, true>(a, stream);
-    return wide ? launch_waves<D, DT, CAUSAL, 8, false>(a, stream) : launch_waves<D, DT, CAUSAL, 4, false>(a, stream);
+        return wide ? launch_waves<D, DT, CAUSAL, 8, true>(a, stream, cus)
+                    : launch_waves<D, DT, CAUSAL, 4, true>(a, stream, cus);
+    return wide ? launch_waves<D, DT, CAUSAL, 8, false>(a, stream, cus)
+                : launch_waves<D, DT, CAUSAL, 4, false>(a, stream, cus);
 }
 
 template <int D, int DT>
-hipError_t dispatch_causal(const FwdArgs& a, int causal, hipStream_t s) {
-    return causal ? launch<D, DT, true>(a, s) : launch<D, DT, false>(a, s);
+hipError_t dispatch_causal(const FwdArgs& a, int causal, hipStream_t s, int cus) {
+    return causal ? launch<D, DT, true>(a, s, cus) : launch<D, DT, false>(a, s, cus);
 }
 
 template <int D>
-hipError_t dispatch_dtype(const FwdArgs& a, int dtype, int causal, hipStream_t s) {
-    return dtype == ATTN_BF16 ? dispatch_causal<D, ATTN_BF16>(a, causal, s) : dispatch_causal<D, ATTN_F16>(a, causal, s);
+hipError_t dispatch_dtype(const FwdArgs& a, int dtype, int causal, hipStream_t s, int cus) {
+    return dtype == ATTN_BF16 ? dispatch_causal<D, ATTN_BF16>(a, causal, s, cus)
+                              : dispatch_causal<D, ATTN_F16>(a, causal, s, cus);
 }
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_ok[kMaxDevices];   // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_cus[kMaxDevices];       // compute units, once known
 
-int check_device() {
+// ATTN_OK when the current device is a gfx950; *cus receives its compute-unit count
+int check_device(int* cus) {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_ERR_DEVICE;
     if (dev < kMaxDevices) {
-        const int st = g_arch_ok[dev].load(std::memory_order_relaxed);
-        if (st == 1) return ATTN_OK;
+        const int st = g_arch_ok[dev].load(std::memory_order_acquire);
+        if (st == 1) {
+            *cus = g_cus[dev].load(std::memory_order_relaxed);
+            return ATTN_OK;
+        }
         if (st == 2) return ATTN_ERR_DEVICE;
     }
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_DEVICE;
     const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-    if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    *cus = prop.multiProcessorCount;
+    if (dev < kMaxDevices) {
+        g_cus[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+        g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_release);
+    }
     return ok ? ATTN_OK : ATTN_ERR_DEVICE;
 }
 
@@ -667,7 +822,8 @@ int fwd(const void* q, const void* k, const void* v, void* out, float* lse, int 
                 overlaps(lse, lse_bytes, v, tensor_bytes) || overlaps(lse, lse_bytes, out, tensor_bytes)))
         return ATTN_ERR_ALIAS;
 
-    const int dev_status = check_device();
+    int cus = 0;
+    const int dev_status = check_device(&cus);
     if (dev_status != ATTN_OK) return dev_status;
 
     FwdArgs a;
@@ -689,9 +845,9 @@ int fwd(const void* q, const void* k, const void* v, void* out, float* lse, int 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
     switch (d) {
-        case 64: err = dispatch_dtype<64>(a, dtype, causal, s); break;
-        case 80: err = dispatch_dtype<80>(a, dtype, causal, s); break;
-        default: err = dispatch_dtype<128>(a, dtype, causal, s); break;
+        case 64: err = dispatch_dtype<64>(a, dtype, causal, s, cus); break;
+        case 80: err = dispatch_dtype<80>(a, dtype, causal, s, cus); break;
+        default: err = dispatch_dtype<128>(a, dtype, causal, s, cus); break;
     }
     return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }

@@ -35,6 +35,7 @@
 #include <cstring>
 
 #include "gemm.h"
+#include "lds_load.h"
 
 namespace {
 
@@ -244,13 +245,11 @@ struct Tile {
         {
             const unsigned char* base = g.a + (size_t)m0 * (size_t)g.lda + (size_t)k0 * 2;
             const int bytes = (int)((rows_a - 1) * g.lda + (long long)krem * 2);
-            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, 0x00020000);
+            const eta_desc_t desc = buffer_desc(base, bytes);
             const unsigned vo = kc * 8 < krem ? loff_a : 0x80000000u;   // chunks past K read as zero
 #pragma unroll
             for (int it = 0; it < C::ROUNDS; ++it) {
-                const unsigned dst = region + C::AOFF + (unsigned)((it * C::NT + wave * 64) * 16);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_bytes)(size_t)dst,
-                                                         16, vo, it * rstep_a, 0, 0);
+                load_lds16(desc, vo, (unsigned)(it * rstep_a), region + C::AOFF + (unsigned)((it * C::NT + wave * 64) * 16));
             }
         }
         if constexpr (BKN) {
@@ -262,23 +261,19 @@ struct Tile {
             const unsigned char* base = g.b + (size_t)k0 * (size_t)g.ldb + (size_t)n0 * 2;
             const int kr = min(krem, C::BK);
             const int bytes = (int)((kr - 1) * g.ldb + (((long long)rows_b * 2 + 15) & ~15LL));
-            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, 0x00020000);
+            const eta_desc_t desc = buffer_desc(base, bytes);
 #pragma unroll
             for (int it = 0; it < C::ROUNDS; ++it) {
-                const unsigned dst = region + C::BOFF + (unsigned)((it * C::NT + wave * 64) * 16);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_bytes)(size_t)dst,
-                                                         16, loff_b, it * rstep_b, 0, 0);
+                load_lds16(desc, loff_b, (unsigned)(it * rstep_b), region + C::BOFF + (unsigned)((it * C::NT + wave * 64) * 16));
             }
         } else {
             const unsigned char* base = g.b + (size_t)n0 * (size_t)g.ldb + (size_t)k0 * 2;
             const int bytes = (int)((rows_b - 1) * g.ldb + (long long)krem * 2);
-            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, 0x00020000);
+            const eta_desc_t desc = buffer_desc(base, bytes);
             const unsigned vo = kc * 8 < krem ? loff_b : 0x80000000u;
 #pragma unroll
             for (int it = 0; it < C::ROUNDS; ++it) {
-                const unsigned dst = region + C::BOFF + (unsigned)((it * C::NT + wave * 64) * 16);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_bytes)(size_t)dst,
-                                                         16, vo, it * rstep_b, 0, 0);
+                load_lds16(desc, vo, (unsigned)(it * rstep_b), region + C::BOFF + (unsigned)((it * C::NT + wave * 64) * 16));
             }
         }
     }
@@ -376,8 +371,6 @@ struct Tile {
 
 #endif  // __HIP_DEVICE_COMPILE__
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 template <int DT, bool BKN, int WAVES, int WAVES_N, int BK, int STAGES>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
