@@ -308,8 +308,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int qw0 = q0 + 32 * wave;
         const int qi = qw0 + st.n;
         // the query's Q and dO rows (B operands of S^T and dP^T), its lse and D
+        // (loaded raw: no arithmetic on them before the first tile loads are
+        // issued, so their latency overlaps those loads)
         u32x4_t qf[KSTEPS], df[KSTEPS];
-        float lse2 = 0.f, dlt = 0.f;
+        float lse_raw = 0.f, dlt = 0.f;
         if (qi < N) {
             const u32x4_t* qs = a.q + hoff + (size_t)qi * CPR + st.hf;
             const u32x4_t* ds = a.dout + hoff + (size_t)qi * CPR + st.hf;
@@ -318,7 +320,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 qf[ks] = qs[2 * ks];
                 df[ks] = ds[2 * ks];
             }
-            lse2 = a.lse[(size_t)bh * N + qi] * kLog2e;
+            lse_raw = a.lse[(size_t)bh * N + qi];
             dlt = a.delta[(size_t)bh * N + qi];
         } else {
 #pragma unroll
@@ -330,6 +332,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
         const int kend = CAUSAL ? min(N, q0 + C::OWN) : N;
         const int nt = (kend + C::BT - 1) / C::BT;
+        float nlse2 = 0.f;                             // -lse log2(e), set once the first tiles are issued
         auto step = [&](int stg, int j) {
             if (j + 1 < nt) {
                 st.issue(kb, N, (j + 1) * C::BT, stg ^ 1, 0);
@@ -357,7 +360,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
                         const int sb = kk >> 1, reg = 8 * (kk & 1) + i;
-                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][reg], a.c, -lse2));
+                        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][reg], a.c, nlse2));
                         float ds = p * (dp[sb][reg] - dlt);
                         if (edge && 32 * sb + 16 * (reg >> 3) + (reg & 7) > hi) ds = 0.f;
                         v[i] = ds;
@@ -377,6 +380,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         st.issue(vb, N, 0, 0, 1);
         wait_loads();
         __syncthreads();
+        // the empty asm keeps the compiler from scaling lse (and so waiting for
+        // its load) before the tile loads above are issued
+        asm volatile("" : "+v"(lse_raw));
+        nlse2 = -lse_raw * kLog2e;
         for (int j = 0; j < nt; j += 2) {
             step(0, j);
             if (j + 1 < nt) step(1, j + 1);

@@ -274,7 +274,13 @@ struct Wave {
         if (qi < N) {
             const u32x4_t* src = a.q + hoff + (size_t)qi * CPR + hf;
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = src[2 * ks] ^ a.qsign;
+            for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = src[2 * ks];
+            // only a negative scale flips Q's sign; with a positive one the loads
+            // are not waited for here and overlap the first K/V tile loads
+            if (a.qsign) {
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] ^= a.qsign;
+            }
         } else {
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = u32x4_t{0, 0, 0, 0};
