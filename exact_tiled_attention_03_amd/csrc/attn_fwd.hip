@@ -173,6 +173,7 @@ template <int D, int WAVES_, int STAGES_ = 2> struct Cfg {
     static_assert(DBLK <= GPR, "transpose reads of the padded head dim stay inside a row");
     static_assert(STAGES == 3 || VOFF + 2 * TILEB <= 65536, "LDS offsets fit the 16-bit immediate");
     static_assert(LDS <= 160 * 1024, "LDS");
+    static_assert(WAVES * 32 * ROWB <= LDS, "the epilogue's per-wave O slices fit in the stages");
 };
 
 typedef __fp16 lds_v4h_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
@@ -468,25 +469,39 @@ struct Wave {
         }
     }
 
-    // O = acc / l rounded to the input type; lse = ln2 * (m + log2 l)
+    // O = acc / l rounded to the input type; lse = ln2 * (m + log2 l).  The wave's
+    // 32 x D block goes through its own slice of LDS (32 rows of ROWB bytes, the
+    // 16-byte chunk c of row r at c ^ (r % CPRP)) so that the global stores are
+    // whole rows: each store instruction writes 64/CPRP consecutive rows.  Only
+    // called when no wave reads the K/V stages and no tile load is in flight
+    // (after the last barrier of a query tile, before the next one's first).
     __device__ __forceinline__ void finish(const FwdArgs& a, int bh) {
         if (qw0 >= N) return;
         const float ltot = pair_sum(l);
-        if (qi >= N) return;
-        const float inv = 1.0f / ltot;
-        uint16_t* orow = a.o + ((size_t)bh * N + qi) * D;
+        const float inv = 1.0f / ltot;   // rows past N are never stored
+        const unsigned slice = lds0 + (unsigned)(wave * 32 * C::ROWB);
 #pragma unroll
         for (int db = 0; db < DBLK; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int d0 = db * 32 + 8 * g + 4 * hf;
-                if (d0 < D) {
+                const int c = 4 * db + g;                      // 16-byte chunk: d = 8c .. 8c+7, this lane's half hf
+                if (c < CPR) {
                     const u32x2_t w = {E::pack2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv),
                                        E::pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
-                    *reinterpret_cast<u32x2_t*>(orow + d0) = w;
+                    *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(
+                        (lds_bytes)(size_t)(slice + n * C::ROWB + ((c ^ (n % C::CPRP)) * 16) + 8 * hf)) = w;
                 }
             }
-        if (a.lse != nullptr && hf == 0) a.lse[(size_t)bh * N + qi] = (m + __builtin_amdgcn_logf(ltot)) * kLn2;
+        constexpr int RPR = 64 / C::CPRP;                     // rows per store round
+        const int rr = lane / C::CPRP, c = lane % C::CPRP;
+        uint16_t* obase = a.o + ((size_t)bh * N + qw0) * D;
+#pragma unroll
+        for (int k = 0; k < 32 / RPR; ++k) {
+            const int r = k * RPR + rr;
+            const u32x4_t v = lds_read16(slice + r * C::ROWB + ((c ^ (r % C::CPRP)) * 16));
+            if (c < CPR && qw0 + r < N) *reinterpret_cast<u32x4_t*>(obase + (size_t)r * D + 8 * c) = v;
+        }
+        if (a.lse != nullptr && hf == 0 && qi < N) a.lse[(size_t)bh * N + qi] = (m + __builtin_amdgcn_logf(ltot)) * kLn2;
     }
 };
 
@@ -663,6 +678,7 @@ void attn_fwd_kernel(FwdArgs a) {
             continue;
         }
 
+        if (!first) __syncthreads();                       // every wave has left the previous item's epilogue
         // one step: prefetch tile j+1 into the other stage, compute tile j, sync.
         // The wave raises its priority while it issues the score MFMAs, so the
         // matrix pipe is fed as soon as it frees up while the other wave on the
