@@ -125,6 +125,7 @@ struct Cfg {
     static_assert(WAVES % WAVES_N == 0 && WM % 32 == 0 && WN % 32 == 0, "wave layouts");
     static_assert((NT / CPRK / RPL) % CPRK == 0 && (NT / 32) % 8 == 0, "load rounds keep every lane's swizzle");
     static_assert(LDS <= 160 * 1024, "LDS");
+    static_assert(WAVES * WM * WN * 2 <= LDS && WN == 128, "the epilogue's per-wave C slices (rows of 256 bytes) fit in the stages");
 };
 using Shape = Cfg<4, 2, 64, 2>;   // the tile shape (BM, BN, GROUP_M) shared by every configuration
 
@@ -138,6 +139,7 @@ struct GemmArgs {
     int act;
     int tm, tn;                  // tile rows (of M) and tile columns (of N)
     int c_vec;                   // 8-byte C stores allowed (c and ldc 8-byte aligned)
+    int c_vec16;                 // 16-byte C stores allowed (c and ldc 16-byte aligned)
 };
 
 typedef __fp16 lds_v4h_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
@@ -329,7 +331,79 @@ struct Tile {
     }
 
     // bias, activation, rounding and the store of this wave's 128 x 128 block
+    // bias + activation of one accumulator quad: C[m][n .. n+3] for this lane
+    __device__ __forceinline__ void epilogue_values(const GemmArgs& g, int nb, int gq, int mb, const float (&bias)[4],
+                                                    float (&v)[4]) const {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float z = acc[nb][mb][4 * gq + j] + bias[j];
+            if (g.act == GEMM_ACT_RELU) z = fmaxf(z, 0.f);
+            else if (g.act == GEMM_ACT_GELU_TANH) z = gelu_tanh(z);
+            v[j] = z;
+        }
+    }
+
+    __device__ __forceinline__ void load_bias(const GemmArgs& g, int n, float (&bias)[4]) const {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) bias[j] = 0.f;
+        if (g.bias) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (n + j < g.N) bias[j] = E::get(g.bias + (size_t)(n + j) * 2);
+        }
+    }
+
+    // Bias, activation, rounding and the stores of C.  With 16-byte aligned C
+    // the wave's WM x WN block first goes to its own slice of the (then unused)
+    // LDS stages, 256-byte rows with the 16-byte chunk c of row r at c ^ (r % 16),
+    // and is stored as whole row segments: each store instruction writes 256
+    // contiguous bytes of four rows instead of 16 bytes of 32 rows.
     __device__ __forceinline__ void finish(const GemmArgs& g) const {
+        if (!g.c_vec16) {
+            finish_direct(g);
+            return;
+        }
+        __syncthreads();                                  // every wave has read its last operands
+        const unsigned slice = lds0 + (unsigned)(wave * C::WM * C::WN * 2);
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int n = n0 + wn * C::WN + nb * 32 + 8 * gq + 4 * hf;
+                float bias[4];
+                load_bias(g, n, bias);
+                const int c = nb * 4 + gq;                // 16-byte chunk of the slice row
+#pragma unroll
+                for (int mb = 0; mb < C::MB; ++mb) {
+                    float v[4];
+                    epilogue_values(g, nb, gq, mb, bias, v);
+                    const int r = mb * 32 + l32;
+                    *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(
+                        (lds_bytes)(size_t)(slice + r * 256 + ((c ^ (r % 16)) * 16) + 8 * hf)) =
+                        u32x2_t{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
+                }
+            }
+        const int c = lane % 16, rq = lane / 16;
+        const int n = n0 + wn * C::WN + 8 * c;
+#pragma unroll
+        for (int k = 0; k < C::WM / 4; ++k) {
+            const int r = 4 * k + rq;
+            const int m = m0 + wm * C::WM + r;
+            const u32x4_t v = lds_read16(slice + r * 256 + ((c ^ (r % 16)) * 16));
+            if (m >= g.M || n >= g.N) continue;
+            unsigned char* dst = g.c + (size_t)m * (size_t)g.ldc + (size_t)n * 2;
+            if (n + 7 < g.N) {
+                *reinterpret_cast<u32x4_t*>(dst) = v;
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (n + j < g.N) reinterpret_cast<uint16_t*>(dst)[j] = (uint16_t)(v[j / 2] >> (16 * (j % 2)));
+            }
+        }
+    }
+
+    // the same values stored straight from the accumulator layout (any C alignment)
+    __device__ __forceinline__ void finish_direct(const GemmArgs& g) const {
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) {
 #pragma unroll
@@ -337,24 +411,14 @@ struct Tile {
                 // accumulator registers 4 gq .. 4 gq + 3 of a lane hold rows
                 // n = nb*32 + 8 gq + 4 hf + (0..3) of C^T, i.e. columns of C
                 const int n = n0 + wn * C::WN + nb * 32 + 8 * gq + 4 * hf;
-                float bias[4] = {0.f, 0.f, 0.f, 0.f};
-                if (g.bias) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (n + j < g.N) bias[j] = E::get(g.bias + (size_t)(n + j) * 2);
-                }
+                float bias[4];
+                load_bias(g, n, bias);
 #pragma unroll
                 for (int mb = 0; mb < C::MB; ++mb) {
                     const int m = m0 + wm * C::WM + mb * 32 + l32;
                     if (m >= g.M || n >= g.N) continue;
                     float v[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        float z = acc[nb][mb][4 * gq + j] + bias[j];
-                        if (g.act == GEMM_ACT_RELU) z = fmaxf(z, 0.f);
-                        else if (g.act == GEMM_ACT_GELU_TANH) z = gelu_tanh(z);
-                        v[j] = z;
-                    }
+                    epilogue_values(g, nb, gq, mb, bias, v);
                     unsigned char* dst = g.c + (size_t)m * (size_t)g.ldc + (size_t)n * 2;
                     if (g.c_vec && n + 3 < g.N) {
                         *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{E::pack2(v[0], v[1]), E::pack2(v[2], v[3])};
@@ -508,6 +572,7 @@ extern "C" int gemm_bias_act(const void* a, long long lda, const void* b, long l
     g.tm = (int)tm;
     g.tn = (int)tn;
     g.c_vec = ((uintptr_t)c % 8 == 0) && (ldc % 4 == 0);
+    g.c_vec16 = ((uintptr_t)c % 16 == 0) && (ldc % 8 == 0);
     return launch<ETA_GEMM_WAVES, ETA_GEMM_WAVES_N, ETA_GEMM_BK, ETA_GEMM_STAGES>(g, dtype, bkn,
                                                                                  static_cast<hipStream_t>(stream)) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
