@@ -266,13 +266,16 @@ struct Wave {
     }
 
     // start a query tile: this wave's rows begin at qw0_
+    // LOADQ false: the Q fragments come later from q_issue / q_read
+    template <bool LOADQ = true>
     __device__ __forceinline__ void begin(const FwdArgs& a, int bh, int qw0_) {
         qw0 = qw0_;
         qi = qw0 + n;
         const size_t hoff = (size_t)bh * (size_t)N * CPR;   // head offset in 16-byte chunks
         kbase = reinterpret_cast<const unsigned char*>(a.k + hoff);
         vbase = reinterpret_cast<const unsigned char*>(a.v + hoff);
-        if (qi < N) {
+        if (!LOADQ) {
+        } else if (qi < N) {
             const u32x4_t* src = a.q + hoff + (size_t)qi * CPR + hf;
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = src[2 * ks];
@@ -302,6 +305,32 @@ struct Wave {
 #pragma unroll
         for (int it = 0; it < C::IT; ++it)
             load_lds16(desc, is_v ? vvo[it] : kvo[it], 0, region + (unsigned)(slot_base(it) * 16));
+    }
+
+    // This wave's 32 Q rows (qw0 ..) into its LDS slice by direct loads: 32 rows of
+    // ROWB bytes, logical 16-byte chunk c of row r at physical c ^ (r % CPRP); rows
+    // at or past N and chunks past the head dim read as zero.  Each load
+    // instruction moves 1 KB of consecutive rows (a register load of the
+    // fragments touches 32 rows per instruction).
+    __device__ __forceinline__ void q_issue(const FwdArgs& a, int bh, unsigned slice) const {
+        const unsigned char* base = reinterpret_cast<const unsigned char*>(a.q + ((size_t)bh * N + qw0) * CPR);
+        const eta_desc_t desc = buffer_desc(base, max(0, (N - qw0) * D * 2));
+#pragma unroll
+        for (int it = 0; it < 32 * C::CPRP / 64; ++it) {
+            const int slot = it * 64 + lane, r = slot / C::CPRP, c = (slot % C::CPRP) ^ (r % C::CPRP);
+            load_lds16(desc, c < CPR ? (unsigned)(r * D * 2 + c * 16) : 0x80000000u, 0, slice + (unsigned)(it * 1024));
+        }
+    }
+
+    // the Q^T fragments (score B operands) from the slice, once q_issue's loads have landed
+    __device__ __forceinline__ void q_read(const FwdArgs& a, unsigned slice) {
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks)
+            qf[ks] = lds_read16(slice + n * C::ROWB + (((2 * ks + hf) ^ (n % C::CPRP)) * 16));
+        if (a.qsign) {
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] ^= a.qsign;
+        }
     }
 
     // first slot of load round `it` for this wave
@@ -533,7 +562,11 @@ void attn_fwd_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
     constexpr int STAGES = fwd_stages<WAVES, WIN>();
     using C = Cfg<D, WAVES, STAGES>;
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS];
+    // the two-group schedule adds room for the Q slices of waves 4-7 (waves 0-3
+    // use the K and V areas of stage 2, free while a query tile's loads start)
+    constexpr int QEXTRA = fwd_ping<WAVES, WIN>() ? 4 * 32 * C::ROWB : 0;
+    static_assert(C::LDS + QEXTRA <= 160 * 1024, "LDS");
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS + QEXTRA];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     Wave<D, DT, CAUSAL, WAVES, WIN, STAGES> w;
@@ -551,7 +584,7 @@ void attn_fwd_kernel(FwdArgs a) {
     for (int item = 0; item < nitems; ++item, first = false) {
         const int qt = CAUSAL ? (item == 0 ? a.nqt - 1 - grp : grp) : grp;
         const int q0 = qt * C::BM;
-        w.begin(a, bh, q0 + 32 * wave);
+        w.template begin<!fwd_ping<WAVES, WIN>()>(a, bh, q0 + 32 * wave);
         // key tiles jlo .. nt-1: up to the last query (causal) or its band's end,
         // from the first query's band start
         const int win = WIN ? a.window : 0;
@@ -616,6 +649,14 @@ void attn_fwd_kernel(FwdArgs a) {
                 if (!g0) wait_loads();                      // slot 2u+2 ends (group 1): tile u+2 landed
                 __syncthreads();
             };
+            // this wave's Q slice: stage 2's K area (waves 0, 1), its V area (2, 3) or
+            // the extra room past the stages (4-7); stage 2 first receives a tile
+            // after the barrier below
+            const unsigned lds_base = (unsigned)(size_t)(lds_bytes)smem;
+            const unsigned qslice = lds_base + (unsigned)((wave < 2   ? C::KOFF + 2 * C::TILEB + wave * 32 * C::ROWB
+                                                           : wave < 4 ? C::VOFF + 2 * C::TILEB + (wave - 2) * 32 * C::ROWB
+                                                                      : C::LDS + (wave - 4) * 32 * C::ROWB));
+            if (w.qw0 < a.N) w.q_issue(a, bh, qslice);
             w.issue(false, jlo, 0);
             w.issue(true, jlo, 0);
             if (T > 1) {
@@ -623,6 +664,7 @@ void attn_fwd_kernel(FwdArgs a) {
                 w.issue(true, jlo + 1, 1);
             }
             wait_loads();
+            w.q_read(a, qslice);                           // this wave's own loads: no barrier needed
             __syncthreads();
             if (w.active(jlo)) w.template score<0>(s);
             if (!g0) __syncthreads();
