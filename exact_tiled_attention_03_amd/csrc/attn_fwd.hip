@@ -59,6 +59,16 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
+// the epilogue's O stores bypass L2 allocation (O is written once and not read back here)
+#ifndef ETA_FWD_NT_STORE
+#define ETA_FWD_NT_STORE 1
+#endif
+
+// Q rows (read once) are loaded with the non-temporal hint
+#ifndef ETA_FWD_NT_Q
+#define ETA_FWD_NT_Q 0
+#endif
+
 // log2 headroom before the reference max is raised (see Wave::prepare)
 #ifndef ETA_RESCALE_TH
 #define ETA_RESCALE_TH 8.0f
@@ -318,7 +328,11 @@ struct Wave {
 #pragma unroll
         for (int it = 0; it < 32 * C::CPRP / 64; ++it) {
             const int slot = it * 64 + lane, r = slot / C::CPRP, c = (slot % C::CPRP) ^ (r % C::CPRP);
+#if ETA_FWD_NT_Q
+            load_lds16_nt(desc, c < CPR ? (unsigned)(r * D * 2 + c * 16) : 0x80000000u, 0, slice + (unsigned)(it * 1024));
+#else
             load_lds16(desc, c < CPR ? (unsigned)(r * D * 2 + c * 16) : 0x80000000u, 0, slice + (unsigned)(it * 1024));
+#endif
         }
     }
 
@@ -528,7 +542,13 @@ struct Wave {
         for (int k = 0; k < 32 / RPR; ++k) {
             const int r = k * RPR + rr;
             const u32x4_t v = lds_read16(slice + r * C::ROWB + ((c ^ (r % C::CPRP)) * 16));
-            if (c < CPR && qw0 + r < N) *reinterpret_cast<u32x4_t*>(obase + (size_t)r * D + 8 * c) = v;
+            if (c < CPR && qw0 + r < N) {
+#if ETA_FWD_NT_STORE
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(obase + (size_t)r * D + 8 * c));
+#else
+                *reinterpret_cast<u32x4_t*>(obase + (size_t)r * D + 8 * c) = v;
+#endif
+            }
         }
         if (a.lse != nullptr && hf == 0 && qi < N) a.lse[(size_t)bh * N + qi] = (m + __builtin_amdgcn_logf(ltot)) * kLn2;
     }

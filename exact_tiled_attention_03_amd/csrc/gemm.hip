@@ -96,6 +96,10 @@ template <> struct Elem<ATTN_BF16> {
 // BK rows (k) of BN values of n (512 bytes); its 64-byte granule g of row r
 // sits at g ^ (r % 8), so the transpose reads of 16 lanes (4 rows x 4 granule
 // offsets) spread over the banks.
+// C rows are stored with the non-temporal hint (written once, not read back)
+#ifndef ETA_GEMM_NT_STORE
+#define ETA_GEMM_NT_STORE 1
+#endif
 #ifndef ETA_GEMM_GROUP_M
 #define ETA_GEMM_GROUP_M 4
 #endif
@@ -393,7 +397,11 @@ struct Tile {
             if (m >= g.M || n >= g.N) continue;
             unsigned char* dst = g.c + (size_t)m * (size_t)g.ldc + (size_t)n * 2;
             if (n + 7 < g.N) {
+#if ETA_GEMM_NT_STORE
+                __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst));
+#else
                 *reinterpret_cast<u32x4_t*>(dst) = v;
+#endif
             } else {
 #pragma unroll
                 for (int j = 0; j < 8; ++j)

@@ -35,6 +35,14 @@ __device__ __forceinline__ void load_lds16(const eta_desc_t& desc, unsigned voff
                  : "memory");
 }
 
+// the same for data read once (the non-temporal hint keeps it from displacing
+// lines that other work-groups will read again)
+__device__ __forceinline__ void load_lds16_nt(const eta_desc_t& desc, unsigned voff, unsigned soff, unsigned lds_dst) {
+    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen nt lds" ::"v"(voff), "s"(desc),
+                 "s"(__builtin_amdgcn_readfirstlane(soff)), "s"(__builtin_amdgcn_readfirstlane(lds_dst))
+                 : "memory");
+}
+
 __device__ __forceinline__ void load_lds4(const eta_desc_t& desc, unsigned voff, unsigned lds_dst) {
     asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(desc),
                  "s"(__builtin_amdgcn_readfirstlane(lds_dst))
