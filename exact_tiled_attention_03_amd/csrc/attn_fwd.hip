@@ -604,7 +604,10 @@ void attn_fwd_kernel(FwdArgs a) {
     for (int item = 0; item < nitems; ++item, first = false) {
         const int qt = CAUSAL ? (item == 0 ? a.nqt - 1 - grp : grp) : grp;
         const int q0 = qt * C::BM;
-        w.template begin<!fwd_ping<WAVES, WIN>()>(a, bh, q0 + 32 * wave);
+        // Q rows through LDS (q_issue / q_read) in the two-group kernel and in the
+        // 4-wave two-stage one (whose stage 1 is free until the first step)
+        constexpr bool QLDS = fwd_ping<WAVES, WIN>() || (STAGES == 2 && WAVES == 4);
+        w.template begin<!QLDS>(a, bh, q0 + 32 * wave);
         // key tiles jlo .. nt-1: up to the last query (causal) or its band's end,
         // from the first query's band start
         const int win = WIN ? a.window : 0;
@@ -764,9 +767,19 @@ void attn_fwd_kernel(FwdArgs a) {
             wait_loads();
             __syncthreads();
         };
+        // the Q slices of the 4-wave kernel: stage 1's K area (waves 0, 1) and V
+        // area (2, 3); stage 1 first receives a tile after the barrier below
+        const unsigned qslice = (unsigned)(size_t)(lds_bytes)smem +
+                                (unsigned)(wave < 2 ? C::KOFF + C::TILEB + wave * 32 * C::ROWB
+                                                    : C::VOFF + C::TILEB + (wave - 2) * 32 * C::ROWB);
+        constexpr bool QLDS2 = STAGES == 2 && WAVES == 4;    // four Q slices fill stage 1
+        if constexpr (QLDS2) {
+            if (w.qw0 < a.N) w.q_issue(a, bh, qslice);
+        }
         w.issue(false, jlo, 0);
         w.issue(true, jlo, 0);
         wait_loads();
+        if constexpr (QLDS2) w.q_read(a, qslice);        // this wave's own loads: no barrier needed
         __syncthreads();
         for (int j = jlo; j < nt; j += 2) {                 // tile j in stage (j - jlo) & 1
             step(std::integral_constant<int, 0>{}, j);
