@@ -523,6 +523,12 @@ struct Wave {
         const float ltot = pair_sum(l);
         const float inv = 1.0f / ltot;   // rows past N are never stored
         const unsigned slice = lds0 + (unsigned)(wave * 32 * C::ROWB);
+        // the lane's addresses are derived here from an opaque copy of the lane
+        // index: computed once before the tile loop they would stay live across
+        // it, and the registers they take get spilled
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int nn = ln & 31, hh = ln >> 5;
 #pragma unroll
         for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -532,21 +538,30 @@ struct Wave {
                     const u32x2_t w = {E::pack2(o[db][4 * g + 0] * inv, o[db][4 * g + 1] * inv),
                                        E::pack2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
                     *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(
-                        (lds_bytes)(size_t)(slice + n * C::ROWB + ((c ^ (n % C::CPRP)) * 16) + 8 * hf)) = w;
+                        (lds_bytes)(size_t)(slice + nn * C::ROWB + ((c ^ (nn & (C::CPRP - 1))) * 16) + 8 * hh)) = w;
                 }
             }
         constexpr int RPR = 64 / C::CPRP;                     // rows per store round
-        const int rr = lane / C::CPRP, c = lane % C::CPRP;
+        const int rr = ln / C::CPRP, c = ln % C::CPRP;
         uint16_t* obase = a.o + ((size_t)bh * N + qw0) * D;
+        // every round's row read first, then the stores back to back
+        u32x4_t v[32 / RPR];
 #pragma unroll
         for (int k = 0; k < 32 / RPR; ++k) {
             const int r = k * RPR + rr;
-            const u32x4_t v = lds_read16(slice + r * C::ROWB + ((c ^ (r % C::CPRP)) * 16));
+            v[k] = lds_read16(slice + r * C::ROWB + ((c ^ (r & (C::CPRP - 1))) * 16));
+        }
+#pragma unroll
+        for (int k = 0; k < 32 / RPR; ++k) asm volatile("" : "+v"(v[k]));
+#pragma unroll
+        for (int k = 0; k < 32 / RPR; ++k) {
+            const int r = k * RPR + rr;
             if (c < CPR && qw0 + r < N) {
+                u32x4_t* dst = reinterpret_cast<u32x4_t*>(obase + (unsigned)(r * D + 8 * c));
 #if ETA_FWD_NT_STORE
-                __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(obase + (size_t)r * D + 8 * c));
+                __builtin_nontemporal_store(v[k], dst);
 #else
-                *reinterpret_cast<u32x4_t*>(obase + (size_t)r * D + 8 * c) = v;
+                *dst = v[k];
 #endif
             }
         }
