@@ -586,6 +586,10 @@ struct Wave {
 #ifndef ETA_FWD_PING
 #define ETA_FWD_PING 1
 #endif
+// the two-group kernel's first wait of a query tile covers only Q and tile 0's K
+#ifndef ETA_FWD_PWAIT
+#define ETA_FWD_PWAIT 1
+#endif
 template <int WAVES, bool WIN> constexpr bool fwd_ping() { return ETA_FWD_PING && WAVES == 8; }
 template <int WAVES, bool WIN> constexpr int fwd_stages() {
     return fwd_ping<WAVES, WIN>() || (ETA_FWD_RING && WAVES == 8 && !WIN) ? 3 : 2;
@@ -701,11 +705,24 @@ void attn_fwd_kernel(FwdArgs a) {
                 w.issue(false, jlo + 1, 1);
                 w.issue(true, jlo + 1, 1);
             }
+#if ETA_FWD_PWAIT
+            // only Q and tile 0's K are needed for the first scores: tile 0's V and
+            // tile 1 (issued after them) are waited for before the barrier that
+            // ends slot 0 (group 0 in its first tile step, group 1 just below)
+            if (T > 1) wait_vmcnt<3 * C::IT>();
+            else wait_vmcnt<C::IT>();
+#else
             wait_loads();
+#endif
             w.q_read(a, qslice);                           // this wave's own loads: no barrier needed
             __syncthreads();
             if (w.active(jlo)) w.template score<0>(s);
-            if (!g0) __syncthreads();
+            if (!g0) {
+#if ETA_FWD_PWAIT
+                wait_loads();
+#endif
+                __syncthreads();
+            }
             for (int u = 0; u < T; u += 3) {
                 tile(std::integral_constant<int, 0>{}, u);
                 if (u + 1 < T) tile(std::integral_constant<int, 1>{}, u + 1);
