@@ -63,7 +63,7 @@ SOFTMAX_SOURCE = os.path.join(ROOT, "exact_tiled_attention_03_amd", "csrc", "sof
 GEMM_SOURCE = os.path.join(ROOT, "exact_tiled_attention_03_amd", "csrc", "gemm.hip")
 BWD_SOURCE = os.path.join(ROOT, "exact_tiled_attention_03_amd", "csrc", "attn_bwd.hip")
 MERGE_SOURCE = os.path.join(ROOT, "exact_tiled_attention_03_amd", "csrc", "lse_merge.hip")
-BWD_KERNELS = ("attn_bwd_delta_kernel", "attn_bwd_dq_kernel", "attn_bwd_dkdv_kernel")
+BWD_KERNELS = ("attn_bwd_dq_kernel", "attn_bwd_dkdv_kernel")
 METRIC_GEMM = "GEMM + bias + activation TFLOP/s (2*M*N*K) and % of bf16 MFMA peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 

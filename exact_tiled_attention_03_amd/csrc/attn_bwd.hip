@@ -7,12 +7,13 @@
 // dQ = scale dS K, dK = scale dS^T Q, dV = P^T dO.  As in the forward, the N x N
 // matrices are produced one tile at a time in registers and never reach HBM.
 //
-// Three kernels:
-//  * delta:  D_i from O and dO (HBM-bound, one 16-lane group per row);
+// Two kernels:
 //  * dq:     a work-group owns 128 query rows (32 per wave) and walks the key
 //            tiles like the forward: S^T = K Q^T and dP^T = V dO^T on MFMA with
 //            the query's Q and dO rows in registers, dS^T formed in registers,
-//            then dQ^T += K^T dS^T with K^T read through the transpose load;
+//            then dQ^T += K^T dS^T with K^T read through the transpose load.
+//            It first forms D_i from the query's O and dO rows and writes it
+//            to `delta` for the second kernel;
 //  * dkdv:   a work-group owns 128 keys (32 per wave) and walks the query
 //            tiles: S = Q K^T and dP = dO V^T with the key's K and V rows in
 //            registers, then dV^T += dO^T P and dK^T += Q^T dS with dO^T and Q^T
@@ -256,32 +257,6 @@ struct Streams {
 
 #endif  // __HIP_DEVICE_COMPILE__
 
-// ---- delta: D_i = sum_c dO_ic O_ic ---------------------------------------------
-template <int D, int DT>
-__global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdArgs a) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    using E = Elem<DT>;
-    constexpr int CPR = D / 8;
-    const int sub = threadIdx.x & 15;
-    const long long rows = (long long)a.BH * a.N;
-    const long long stride = (long long)gridDim.x * 16;
-    for (long long r = ((long long)blockIdx.x * 256 + threadIdx.x) >> 4; r < rows; r += stride) {
-        float s = 0.f;
-        if (sub < CPR) {
-            const u32x4_t x = a.o[r * CPR + sub], y = a.dout[r * CPR + sub];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                s = __builtin_fmaf(E::lo(x[i]), E::lo(y[i]), s);
-                s = __builtin_fmaf(E::hi(x[i]), E::hi(y[i]), s);
-            }
-        }
-#pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o, 16);
-        if (sub == 0) a.delta[r] = s;
-    }
-#endif
-}
-
 // ---- dQ: a work-group owns 128 queries and walks the key tiles --------------------
 template <int D, int DT, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dq_kernel(BwdArgs a) {
@@ -307,24 +282,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int q0 = qt * C::OWN;
         const int qw0 = q0 + 32 * wave;
         const int qi = qw0 + st.n;
-        // the query's Q and dO rows (B operands of S^T and dP^T), its lse and D
-        // (loaded raw: no arithmetic on them before the first tile loads are
-        // issued, so their latency overlaps those loads)
-        u32x4_t qf[KSTEPS], df[KSTEPS];
-        float lse_raw = 0.f, dlt = 0.f;
+        // the query's Q and dO rows (B operands of S^T and dP^T), its O row (for
+        // D) and lse, loaded raw: no arithmetic on them before the first tile
+        // loads are issued, so their latency overlaps those loads
+        u32x4_t qf[KSTEPS], df[KSTEPS], of[KSTEPS];
+        float lse_raw = 0.f;
         if (qi < N) {
             const u32x4_t* qs = a.q + hoff + (size_t)qi * CPR + st.hf;
             const u32x4_t* ds = a.dout + hoff + (size_t)qi * CPR + st.hf;
+            const u32x4_t* os = a.o + hoff + (size_t)qi * CPR + st.hf;
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
                 qf[ks] = qs[2 * ks];
                 df[ks] = ds[2 * ks];
+                of[ks] = os[2 * ks];
             }
             lse_raw = a.lse[(size_t)bh * N + qi];
-            dlt = a.delta[(size_t)bh * N + qi];
         } else {
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = df[ks] = u32x4_t{0, 0, 0, 0};
+            for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = df[ks] = of[ks] = u32x4_t{0, 0, 0, 0};
         }
         f32x16_t acc[DBLK];
 #pragma unroll
@@ -333,6 +309,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int kend = CAUSAL ? min(N, q0 + C::OWN) : N;
         const int nt = (kend + C::BT - 1) / C::BT;
         float nlse2 = 0.f;                             // -lse log2(e), set once the first tiles are issued
+        float dlt = 0.f;                               // D_i, likewise
         auto step = [&](int stg, int j) {
             if (j + 1 < nt) {
                 st.issue(kb, N, (j + 1) * C::BT, stg ^ 1, 0);
@@ -384,6 +361,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // its load) before the tile loads above are issued
         asm volatile("" : "+v"(lse_raw));
         nlse2 = -lse_raw * kLog2e;
+        // D_i = sum_c dO_ic O_ic: this lane's half of the row, then the other
+        // half's from the lane 32 away; written for the dK/dV kernel and the caller
+        float dpart = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                dpart = __builtin_fmaf(E::lo(df[ks][i]), E::lo(of[ks][i]), dpart);
+                dpart = __builtin_fmaf(E::hi(df[ks][i]), E::hi(of[ks][i]), dpart);
+            }
+        dlt = pair_sum(dpart);
+        if (st.hf == 0 && qi < N) a.delta[(size_t)bh * N + qi] = dlt;
         for (int j = 0; j < nt; j += 2) {
             step(0, j);
             if (j + 1 < nt) step(1, j + 1);
@@ -561,10 +550,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 template <int D, int DT, bool CAUSAL>
 hipError_t launch(BwdArgs a, hipStream_t s) {
     using C = BCfg<D>;
-    const long long rows = (long long)a.BH * a.N;
-    const long long dgroups = (rows + 15) / 16;
-    hipLaunchKernelGGL((attn_bwd_delta_kernel<D, DT>), dim3((unsigned)(dgroups < 65536 ? dgroups : 65536)), dim3(256), 0,
-                       s, a);
     const int ntile = (a.N + C::OWN - 1) / C::OWN;
     a.ntile = ntile;
     a.ngroups = CAUSAL ? (ntile + 1) / 2 : ntile;
