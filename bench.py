@@ -478,7 +478,7 @@ def bench_backward(args, w, causal):
                    "scale": w.scale, "pct_of_mfma_peak": round(100 * value / MFMA_PEAK_TFLOPS, 2),
                    "launch_ms_median": round(statistics.median(per_launch), 5),
                    "launch_ms_min": round(min(per_launch), 5),
-                   "note": "one step = the delta, dQ and dK/dV kernels of one attn_bwd call"},
+                   "note": "one step = the dQ (with D) and dK/dV kernels of one attn_bwd call"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(w.name, causal, 0, BWD_SOURCE, key=f"{w.name}-causal{causal}-backward"),
