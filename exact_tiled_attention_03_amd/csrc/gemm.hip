@@ -97,6 +97,15 @@ template <> struct Elem<ATTN_BF16> {
 // sits at g ^ (r % 8), so the transpose reads of 16 lanes (4 rows x 4 granule
 // offsets) spread over the banks.
 // C rows are stored with the non-temporal hint (written once, not read back)
+// the two-group kernel (below) and whether it spreads each tile's load rounds
+// over its phases instead of issuing them at a phase's start
+#ifndef ETA_GEMM_PP
+#define ETA_GEMM_PP 1
+#endif
+#ifndef ETA_GEMM_SPREAD
+#define ETA_GEMM_SPREAD 1
+#endif
+
 #ifndef ETA_GEMM_NT_STORE
 #define ETA_GEMM_NT_STORE 1
 #endif
@@ -284,6 +293,41 @@ struct Tile {
         }
     }
 
+    // load rounds r0 .. r1-1 of tile j (rounds 0 .. ROUNDS-1 of A, then those of B)
+    __device__ __forceinline__ void issue_rounds(const GemmArgs& g, int j, unsigned stage, int r0, int r1) const {
+        const int k0 = j * C::BK;
+        const int krem = g.K - k0;
+        const unsigned region = lds0 + stage;
+        if (r0 < C::ROUNDS) {
+            const unsigned char* base = g.a + (size_t)m0 * (size_t)g.lda + (size_t)k0 * 2;
+            const eta_desc_t desc = buffer_desc(base, (int)((rows_a - 1) * g.lda + (long long)krem * 2));
+            const unsigned vo = kc * 8 < krem ? loff_a : 0x80000000u;
+#pragma unroll
+            for (int it = 0; it < C::ROUNDS; ++it)
+                if (it >= r0 && it < r1)
+                    load_lds16(desc, vo, (unsigned)(it * rstep_a), region + C::AOFF + (unsigned)((it * C::NT + wave * 64) * 16));
+        }
+        if (r1 > C::ROUNDS) {
+            if constexpr (BKN) {
+                const unsigned char* base = g.b + (size_t)k0 * (size_t)g.ldb + (size_t)n0 * 2;
+                const int kr = min(krem, C::BK);
+                const eta_desc_t desc = buffer_desc(base, (int)((kr - 1) * g.ldb + (((long long)rows_b * 2 + 15) & ~15LL)));
+#pragma unroll
+                for (int it = 0; it < C::ROUNDS; ++it)
+                    if (it + C::ROUNDS >= r0 && it + C::ROUNDS < r1)
+                        load_lds16(desc, loff_b, (unsigned)(it * rstep_b), region + C::BOFF + (unsigned)((it * C::NT + wave * 64) * 16));
+            } else {
+                const unsigned char* base = g.b + (size_t)n0 * (size_t)g.ldb + (size_t)k0 * 2;
+                const eta_desc_t desc = buffer_desc(base, (int)((rows_b - 1) * g.ldb + (long long)krem * 2));
+                const unsigned vo = kc * 8 < krem ? loff_b : 0x80000000u;
+#pragma unroll
+                for (int it = 0; it < C::ROUNDS; ++it)
+                    if (it + C::ROUNDS >= r0 && it + C::ROUNDS < r1)
+                        load_lds16(desc, vo, (unsigned)(it * rstep_b), region + C::BOFF + (unsigned)((it * C::NT + wave * 64) * 16));
+            }
+        }
+    }
+
     // operands of k-step s from the stage at `base` (= lds0 + stage offset):
     // av[nb] is the MFMA A operand (B^T block nb: 32 n x 16 k), bv[mb] the B
     // operand (A^T block mb: 16 k x 32 m)
@@ -331,6 +375,31 @@ struct Tile {
 #pragma unroll
                 for (int mb = 0; mb < C::MB; ++mb) acc[nb][mb] = E::mfma(av[s & 1][nb], bv[s & 1][mb], acc[nb][mb]);
             __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // every operand of the tile in the stage at byte offset `stage`, all KS k-steps;
+    // with j >= 0, tile j's load rounds are issued in between (LOADS / KS per k-step)
+    __device__ __forceinline__ void load_step(const GemmArgs& g, unsigned stage, u32x4_t (&av)[C::KS][C::NB],
+                                              u32x4_t (&bv)[C::KS][C::MB], int j, unsigned jstage) const {
+#pragma unroll
+        for (int s = 0; s < C::KS; ++s) {
+            if (ETA_GEMM_SPREAD && j >= 0) issue_rounds(g, j, jstage, s * C::LOADS / C::KS, (s + 1) * C::LOADS / C::KS);
+            operands(lds0 + stage, s, av[s], bv[s]);
+        }
+    }
+
+    // the tile's MFMAs from operands already in registers; with j >= 0, tile j's
+    // load rounds are issued in between (LOADS / KS per k-step)
+    __device__ __forceinline__ void mma_step(const GemmArgs& g, const u32x4_t (&av)[C::KS][C::NB],
+                                             const u32x4_t (&bv)[C::KS][C::MB], int j, unsigned jstage) {
+#pragma unroll
+        for (int s = 0; s < C::KS; ++s) {
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < C::MB; ++mb) acc[nb][mb] = E::mfma(av[s][nb], bv[s][mb], acc[nb][mb]);
+            if (ETA_GEMM_SPREAD && j >= 0) issue_rounds(g, j, jstage, s * C::LOADS / C::KS, (s + 1) * C::LOADS / C::KS);
         }
     }
 
@@ -481,6 +550,64 @@ void gemm_kernel(GemmArgs g) {
 #endif
 }
 
+// Two wave groups in alternation (8 waves, 2 LDS stages): waves 0-3 and 4-7,
+// one of each on every SIMD, run the same sequence per k tile i,
+//     M(i)  barrier  X(i)  barrier
+// with M(i) = every operand of tile i read from LDS into registers and X(i) =
+// tile i's MFMAs from those registers.  Group 1 passes one extra barrier
+// before its first M and group 0 one after its last X, so between two
+// barriers one wave of a SIMD issues MFMAs while the other reads LDS:
+//     slot 2i:   group 0 M(i),  group 1 X(i-1)
+//     slot 2i+1: group 0 X(i),  group 1 M(i)
+// Tile i+1 is issued at the start of slot 2i (group 0 at the start of M(i),
+// group 1 at the start of X(i-1); its stage last held tile i-1, read in slots
+// 2i-2 and 2i-1) and waited for at the end of slot 2i+1, before its first read
+// in slot 2i+2.
+template <int DT, bool BKN, int WAVES, int WAVES_N, int BK, int STAGES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
+void gemm_kernel_pp(GemmArgs g) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using C = Cfg<WAVES, WAVES_N, BK, STAGES>;
+    static_assert(WAVES == 8 && STAGES == 2, "two groups of four waves, two stages");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS];
+    Tile<DT, BKN, C> t;
+    int tile_m, tile_n;
+    map_tile(g, tile_m, tile_n);
+    t.init(g, (unsigned)(size_t)(lds_bytes)lds, tile_m, tile_n);
+    const int nk = (g.K + C::BK - 1) / C::BK;
+    const bool g0 = t.wave < 4;                      // wave-uniform
+    u32x4_t av[C::KS][C::NB], bv[C::KS][C::MB];
+    // tile 0 from everyone; group 1's share of tile 1 too (group 0 issues its
+    // share at the start of its first M)
+    if (nk > 0) t.issue(g, 0, 0);
+    if (!g0 && nk > 1) {
+        t.issue(g, 1, C::STAGE);
+        wait_vmcnt<C::LOADS>();
+    } else {
+        wait_vmcnt<0>();
+    }
+    __syncthreads();
+    if (!g0) __syncthreads();
+    for (int i = 0; i < nk; ++i) {
+        const unsigned st = (unsigned)(i & 1) * C::STAGE;
+        const int j0 = g0 && i + 1 < nk ? i + 1 : -1;   // group 0: tile i+1 during M(i)
+        const int j1 = !g0 && i + 2 < nk ? i + 2 : -1;  // group 1: tile i+2 during X(i)
+        if (!ETA_GEMM_SPREAD && j0 >= 0) t.issue(g, j0, C::STAGE - st);
+        t.load_step(g, st, av, bv, j0, C::STAGE - st);
+        if (!g0) wait_vmcnt<0>();                    // slot 2i+1 ends (group 1): tile i+1 landed
+        __syncthreads();
+        if (!ETA_GEMM_SPREAD && j1 >= 0) t.issue(g, j1, st);   // slot 2i+2 starts (group 1)
+        __builtin_amdgcn_s_setprio(2);
+        t.mma_step(g, av, bv, j1, st);
+        __builtin_amdgcn_s_setprio(0);
+        if (g0) wait_vmcnt<0>();                     // slot 2i+1 ends (group 0): tile i+1 landed
+        __syncthreads();
+    }
+    if (g0) __syncthreads();
+    t.finish(g);
+#endif
+}
+
 // --- host side ---------------------------------------------------------------
 
 constexpr int kMaxDevices = 64;
@@ -518,9 +645,20 @@ bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a
 #define ETA_GEMM_STAGES 2
 #endif
 
+
 template <int WAVES, int WAVES_N, int BK, int STAGES>
 hipError_t launch(const GemmArgs& g, int dtype, bool bkn, hipStream_t s) {
     const dim3 grid((unsigned)(g.tm * g.tn)), block(64 * WAVES);
+    if constexpr (ETA_GEMM_PP && WAVES == 8 && STAGES == 2) {
+        if (dtype == ATTN_BF16) {
+            if (bkn) hipLaunchKernelGGL((gemm_kernel_pp<ATTN_BF16, true, WAVES, WAVES_N, BK, STAGES>), grid, block, 0, s, g);
+            else hipLaunchKernelGGL((gemm_kernel_pp<ATTN_BF16, false, WAVES, WAVES_N, BK, STAGES>), grid, block, 0, s, g);
+        } else {
+            if (bkn) hipLaunchKernelGGL((gemm_kernel_pp<ATTN_F16, true, WAVES, WAVES_N, BK, STAGES>), grid, block, 0, s, g);
+            else hipLaunchKernelGGL((gemm_kernel_pp<ATTN_F16, false, WAVES, WAVES_N, BK, STAGES>), grid, block, 0, s, g);
+        }
+        return hipGetLastError();
+    }
     if (dtype == ATTN_BF16) {
         if (bkn) hipLaunchKernelGGL((gemm_kernel<ATTN_BF16, true, WAVES, WAVES_N, BK, STAGES>), grid, block, 0, s, g);
         else hipLaunchKernelGGL((gemm_kernel<ATTN_BF16, false, WAVES, WAVES_N, BK, STAGES>), grid, block, 0, s, g);
