@@ -11,12 +11,18 @@
 //
 // gfx950 mapping (not taken from the pages, which target NVIDIA tensor cores):
 //
-//  * 256 x 256 tiles, BK = 64, four waves in a 2 x 2 grid, each wave 128 x 128
-//    = 4 x 4 blocks of v_mfma_f32_32x32x16 (16 fp32 accumulators per lane).
+//  * 256 x 256 tiles, BK = 64, eight waves (two per SIMD) in a 2 (n) x 4 (m)
+//    grid, each wave 128 n x 64 m = 4 x 2 blocks of v_mfma_f32_32x32x16.
+//  * The two waves of a SIMD belong to two groups that alternate between
+//    reading a k tile's operands from LDS into registers and running its
+//    MFMAs from registers (gemm_kernel_pp), so one issues MFMAs while the other
+//    reads LDS; the next tile's loads are spread over both phases.
 //  * The MFMA produces C^T: the A operand is a 32-row block of B^T (n, k) and
 //    the B operand a 32-column block of A^T (k, m).  In the 32 x 32
 //    accumulator layout a lane then owns one m and runs of 4 consecutive n,
-//    so the epilogue stores 8 contiguous bytes of a C row at a time.
+//    so the epilogue stages each wave's block through LDS and stores whole
+//    256-byte row segments (8 contiguous bytes per lane without 16-byte
+//    aligned C).
 //  * A and B tiles go from HBM straight into LDS (buffer loads with the LDS
 //    destination), two stages of 64 KB; rows of 128 bytes, 16-byte chunks
 //    XOR-swizzled by row so the operand reads are free of bank conflicts.
