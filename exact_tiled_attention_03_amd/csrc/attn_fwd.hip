@@ -24,8 +24,10 @@
 //    Those runs are exactly the B operand layout of O^T += V^T P^T, so P goes
 //    from the score accumulator to the P.V operand without leaving the lane.
 //  * K and V tiles go from HBM straight into LDS (buffer loads with the LDS
-//    destination), double-buffered, rows XOR-swizzled for conflict-free reads.
-//    V stays row-major; its P.V operand is read with the gfx950 transpose load.
+//    destination, issued from inline assembly), rows XOR-swizzled for
+//    conflict-free reads: two stages for 4-wave work-groups, a three-stage
+//    ring for 8-wave ones.  V stays row-major; its P.V operand is read with
+//    the gfx950 transpose load.
 //  * Work-groups are remapped so that each XCD (ids are dealt round-robin over
 //    the 8 XCDs) gets a contiguous run of heads, keeping a head's K/V in one
 //    L2.  A causal work-group takes the query-tile pair (i, nqt-1-i), so all
@@ -33,10 +35,12 @@
 //  * exp is evaluated as exp2 with scale*log2(e) folded into one FMA; lse is
 //    returned in natural-log units.
 //
-// Waves run free (no phase coupling): two work-groups share a CU, so on each
-// SIMD one wave's exponentials overlap the other's MFMAs.  Large problems use
-// 8 waves (256 queries) per work-group, halving the K/V loads per query; small
-// ones use 4 waves (128 queries) so that the grid still fills the 256 CUs.
+// Small problems use 4-wave work-groups (128 queries) whose waves run free:
+// two work-groups share a CU, so on each SIMD one wave's exponentials overlap
+// the other's MFMAs, and the grid still fills the 256 CUs.  Large problems use
+// 8-wave work-groups (256 queries, halving the K/V loads per query), resident
+// one per CU, whose two groups of four waves alternate between the softmax
+// half and the matrix half of a key tile (see the kernel).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
