@@ -148,7 +148,7 @@ __device__ __forceinline__ int kperm(int m) {
 
 // Tile configuration shared by the kernels and the host launcher.
 //
-// LDS holds two stages of K and V, each a BN x ROWB byte array written by
+// LDS holds STAGES stages of K and V, each a BN x ROWB byte array written by
 // direct global->LDS loads: one load instruction of a wave fills 1 KB of
 // consecutive 16-byte slots, so rows are unpadded (ROWB = CPRP * 16 with CPRP
 // the chunk count rounded up to a power of two) and bank conflicts are avoided
