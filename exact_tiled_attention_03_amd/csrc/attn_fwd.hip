@@ -470,24 +470,28 @@ struct Wave {
     }
 
     // The matrix half of a step: O^T += V^T P^T for the tile in V stage ST and
-    // S^T = K Q^T for the tile in K stage ST1, in rounds of up to two MFMAs of
-    // each.  The LDS operands of round r+PD are read before round r's MFMAs
-    // (scheduling fences keep the compiler from sinking the reads next to
-    // their MFMAs), so PD+1 rounds of operands are live at a time.
+    // S^T = K Q^T for the tile in K stage ST1, in rounds of up to RS MFMAs of
+    // each (one P.V and one score MFMA by default).  The LDS operands of round
+    // r+PD are read before round r's MFMAs (scheduling fences keep the compiler
+    // from sinking the reads next to their MFMAs), so PD+1 rounds of operands
+    // are live at a time.
 #ifndef ETA_FWD_PD
 #define ETA_FWD_PD 1
 #endif
+#ifndef ETA_FWD_RS
+#define ETA_FWD_RS 1
+#endif
     template <int ST, int ST1>
     __device__ __forceinline__ void pv_score(const u32x4_t (&pf)[KK], f32x16_t (&s)[SB]) {
-        constexpr int NPV = KK * DBLK, NSC = KSTEPS * SB;
-        constexpr int R = ((NPV > NSC ? NPV : NSC) + 1) / 2;
+        constexpr int NPV = KK * DBLK, NSC = KSTEPS * SB, RS = ETA_FWD_RS;
+        constexpr int R = ((NPV > NSC ? NPV : NSC) + RS - 1) / RS;
         constexpr int PD = ETA_FWD_PD < R ? ETA_FWD_PD : R - 1, NB = PD + 1;
-        u32x4_t vo[NB][2], ko[NB][2];
+        u32x4_t vo[NB][RS], ko[NB][RS];
         auto rd = [&](int r) {
             const int b = r % NB;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int pi = 2 * r + i;
+            for (int i = 0; i < RS; ++i) {
+                const int pi = RS * r + i;
                 if (pi < NPV) {
                     const int kk = pi / DBLK, db = pi % DBLK;
                     const u32x2_t lo = lds_read_tr(va[db] + ST * C::TILEB + 16 * kk * C::ROWB);
@@ -507,8 +511,8 @@ struct Wave {
             __builtin_amdgcn_sched_barrier(0);
             const int b = r % NB;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int pi = 2 * r + i;
+            for (int i = 0; i < RS; ++i) {
+                const int pi = RS * r + i;
                 if (pi < NPV) o[pi % DBLK] = E::mfma(vo[b][i], pf[pi / DBLK], o[pi % DBLK]);
                 if (pi < NSC) s[pi % SB] = E::mfma(ko[b][i], qf[pi / SB], s[pi % SB]);
             }
