@@ -53,6 +53,11 @@ typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// the dQ kernel's MFMAs in fenced rounds with their LDS operands read a round ahead
+#ifndef ETA_BWD_DQ_ROUNDS
+#define ETA_BWD_DQ_ROUNDS 1
+#endif
+
 template <int DT> struct Elem;
 
 template <> struct Elem<ATTN_F16> {
@@ -320,6 +325,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 f32x16_t s[2], dp[2];
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb) s[sb] = dp[sb] = f32x16_t{};
+#if ETA_BWD_DQ_ROUNDS
+                {
+                    // rounds of one S and one dP MFMA, the K and V rows of round
+                    // r+1 read before round r's MFMAs (scheduling fences keep them there)
+                    constexpr int R = 2 * KSTEPS;
+                    u32x4_t ko[2], vo[2];
+                    ko[0] = st.row(stg, 0, 0, 0);
+                    vo[0] = st.row(stg, 1, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        if (r + 1 < R) {
+                            ko[(r + 1) & 1] = st.row(stg, 0, (r + 1) & 1, (r + 1) >> 1);
+                            vo[(r + 1) & 1] = st.row(stg, 1, (r + 1) & 1, (r + 1) >> 1);
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
+                        s[r & 1] = E::mfma(ko[r & 1], qf[r >> 1], s[r & 1]);
+                        dp[r & 1] = E::mfma(vo[r & 1], df[r >> 1], dp[r & 1]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+#else
 #pragma unroll
                 for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
@@ -327,6 +353,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                         s[sb] = E::mfma(st.row(stg, 0, sb, ks), qf[ks], s[sb]);
                         dp[sb] = E::mfma(st.row(stg, 1, sb, ks), df[ks], dp[sb]);
                     }
+#endif
                 // dS^T = P^T (dP^T - D); register i of block sb is key kt0 + 32 sb + 16 (i/8) + 8 hf + i%8
                 const bool edge = (CAUSAL && kt0 + C::BT - 1 > qw0) || kt0 + C::BT > N;
                 const int hi = (CAUSAL ? min(qi, N - 1) : N - 1) - (kt0 + 8 * st.hf);
@@ -345,10 +372,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     dsf[kk] = u32x4_t{E::pack2(v[0], v[1]), E::pack2(v[2], v[3]), E::pack2(v[4], v[5]), E::pack2(v[6], v[7])};
                 }
                 // dQ^T += K^T dS^T
+#if ETA_BWD_DQ_ROUNDS
+                {
+                    constexpr int R = 4 * DBLK;
+                    u32x4_t to[2];
+                    to[0] = st.tr(stg, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < R; ++r) {
+                        if (r + 1 < R) to[(r + 1) & 1] = st.tr(stg, 0, (r + 1) / DBLK, (r + 1) % DBLK);
+                        __builtin_amdgcn_sched_barrier(0);
+                        acc[r % DBLK] = E::mfma(to[r & 1], dsf[r / DBLK], acc[r % DBLK]);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+#else
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
                     for (int db = 0; db < DBLK; ++db) acc[db] = E::mfma(st.tr(stg, 0, kk, db), dsf[kk], acc[db]);
+#endif
             }
             wait_loads();
             __syncthreads();
