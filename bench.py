@@ -164,10 +164,11 @@ def traffic_summary(attn_fetch, attn_write, copy_fetch, copy_write, workload, ca
 SETTLE_S = 0.25   # minimum untimed warm-up time: the GPU clock ramps up over the first ~100 ms of load
 
 
-def warm_up(call, steps: int) -> dict:
+def warm_up(call, steps: int, sampler=None) -> dict:
     """Run `steps` untimed warm-up steps, then keep going until SETTLE_S seconds of
-    warm-up have passed, so that the timed steps see a settled clock.  Returns what
-    was done (reported in the JSON line)."""
+    warm-up have passed, so that the timed steps see a settled clock.  The clock
+    sampler, if given, is started for the last 0.1 s.  Returns what was done
+    (reported in the JSON line)."""
     import torch
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -175,11 +176,111 @@ def warm_up(call, steps: int) -> dict:
     torch.cuda.synchronize()
     extra = 0
     while time.perf_counter() - t0 < SETTLE_S:
+        if sampler is not None and sampler._thread is None and time.perf_counter() - t0 >= SETTLE_S - 0.1:
+            sampler.start()
         for _ in range(10):
             call()
         extra += 10
         torch.cuda.synchronize()
+    if sampler is not None and sampler._thread is None:
+        sampler.start()
     return {"steps": steps, "extra_settle_steps": extra, "seconds": round(time.perf_counter() - t0, 3)}
+
+
+class SclkSampler:
+    """Samples the GPU's graphics clock (amdsmi gpu metrics, MHz, per XCD where the
+    driver reports it) from a background thread while kernels run, so the JSON line
+    states the clock the percentages of peak were measured at."""
+
+    def __init__(self, period_s: float = 0.001):
+        import threading
+        self.period_s = period_s
+        self.samples = []
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = None
+        self._handle = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if not handles:
+                raise RuntimeError("amdsmi sees no GPU")
+            self._amdsmi = amdsmi
+            self._handle = handles[0]
+            self._read()   # fail here, not in the thread
+        except Exception as e:   # the clock is context; its absence must not stop the benchmark
+            self.error = f"{type(e).__name__}: {e}"
+            self._handle = None
+
+    def _read(self):
+        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
+        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
+        if clks:
+            return float(sum(clks)) / len(clks)
+        c = m.get("current_gfxclk")
+        return float(c) if isinstance(c, (int, float)) and c > 0 else None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+                if v is not None:
+                    self.samples.append(v)
+            except Exception as e:
+                self.error = f"{type(e).__name__}: {e}"
+                return
+            self._stop.wait(self.period_s)
+
+    def start(self):
+        import threading
+        if self._handle is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def stop(self) -> dict:
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        if not self.samples:
+            return {"median_mhz": None, "samples": 0, "error": self.error or "no samples"}
+        v = sorted(self.samples)
+        return {"median_mhz": round(statistics.median(v), 1), "min_mhz": round(v[0], 1), "max_mhz": round(v[-1], 1),
+                "samples": len(v), "source": "amdsmi gpu metrics current_gfxclks (mean over XCDs), sampled every 1 ms",
+                "window": "the last ~0.1 s of warm-up, the timed steps and the per-launch loop"}
+
+
+def time_steps(call, steps: int, stream) -> dict:
+    """The K timed steps: one event before the first launch and one after the last,
+    with a synchronize on both sides (ms_per_step = elapsed / K, nothing between the
+    launches).  Then a separate loop of K launches, each between its own pair of
+    events, for per-launch statistics (the kernel's own duration for the roofline)."""
+    import torch
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for _ in range(steps):
+        call()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    per_launch = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    return {"ms_per_step": total_ms / steps, "per_launch": per_launch, "launch_ms": statistics.mean(per_launch)}
+
+
+def launch_stats(t: dict) -> dict:
+    pl = sorted(t["per_launch"])
+    return {"launch_ms_mean": round(t["launch_ms"], 5), "launch_ms_median": round(statistics.median(pl), 5),
+            "launch_ms_p95": round(pl[int(0.95 * (len(pl) - 1))], 5), "launch_ms_min": round(pl[0], 5)}
 
 
 def kept_pairs(n: int, causal: int, window: int, rows=None) -> float:
@@ -280,24 +381,11 @@ def bench_softmax(args, w):
     x = aw.make_rows(w.rows, w.cols, w.dtype, w.seed, w.sigma).to(dev)
     y = torch.empty_like(x)
     stream = torch.cuda.current_stream()
-    warm = warm_up(lambda: eta.softmax_rows(x, y, stream=stream), args.warmup)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_begin.record(stream)
-    for i in range(args.steps):
-        starts[i].record(stream)
-        eta.softmax_rows(x, y, stream=stream)
-        ends[i].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-
-    total_ms = t_begin.elapsed_time(t_end)
-    per_launch = [a.elapsed_time(b) for a, b in zip(starts, ends)]
-    ms_per_step = total_ms / args.steps
-    launch_ms = statistics.mean(per_launch)
+    sampler = SclkSampler()
+    warm = warm_up(lambda: eta.softmax_rows(x, y, stream=stream), args.warmup, sampler)
+    t = time_steps(lambda: eta.softmax_rows(x, y, stream=stream), args.steps, stream)
+    sclk = sampler.stop()
+    ms_per_step, launch_ms = t["ms_per_step"], t["launch_ms"]
     nbytes = w.algorithmic_bytes()
     value = nbytes / (ms_per_step * 1e-3) / 1e9
     achieved = nbytes / (launch_ms * 1e-3) / 1e9
@@ -317,9 +405,7 @@ def bench_softmax(args, w):
         "dtype": w.dtype,
         "data": f"synthetic (seeded iid N(0,{w.sigma:g}) x)",
         "config": {"workload": w.name, "rows": w.rows, "cols": w.cols, "layout": "[rows, cols] contiguous",
-                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-                   "launch_ms_median": round(statistics.median(per_launch), 5),
-                   "launch_ms_min": round(min(per_launch), 5)},
+                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2), **launch_stats(t), "sclk": sclk},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(w.name, None, 0, SOFTMAX_SOURCE),
@@ -372,24 +458,11 @@ def bench_gemm(args, w):
     def call():
         eta.gemm_bias_act(a, b, bias, w.act, w.b_layout, c=c, stream=stream)
 
-    warm = warm_up(call, args.warmup)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_begin.record(stream)
-    for i in range(args.steps):
-        starts[i].record(stream)
-        call()
-        ends[i].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-
-    total_ms = t_begin.elapsed_time(t_end)
-    per_launch = [x.elapsed_time(y) for x, y in zip(starts, ends)]
-    ms_per_step = total_ms / args.steps
-    launch_ms = statistics.mean(per_launch)
+    sampler = SclkSampler()
+    warm = warm_up(call, args.warmup, sampler)
+    t = time_steps(call, args.steps, stream)
+    sclk = sampler.stop()
+    ms_per_step, launch_ms = t["ms_per_step"], t["launch_ms"]
     flops = w.flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (launch_ms * 1e-3) / 1e12
@@ -408,9 +481,8 @@ def bench_gemm(args, w):
         "dtype": w.dtype,
         "data": "synthetic (seeded iid N(0,1) A, N(0,1/K) B, N(0,1) bias)",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "b_layout": w.b_layout, "act": w.act,
-                   "bias": w.bias, "pct_of_mfma_peak": round(100 * value / MFMA_PEAK_TFLOPS, 2),
-                   "launch_ms_median": round(statistics.median(per_launch), 5),
-                   "launch_ms_min": round(min(per_launch), 5)},
+                   "bias": w.bias, "pct_of_mfma_peak": round(100 * value / MFMA_PEAK_TFLOPS, 2), **launch_stats(t),
+                   "sclk": sclk},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(w.name, None, 0, GEMM_SOURCE),
@@ -440,23 +512,11 @@ def bench_backward(args, w, causal):
     def call():
         eta.attn_bwd(q, k, v, out, lse, do, dq, dk, dv, delta, causal=bool(causal), scale=w.scale, stream=stream)
 
-    warm = warm_up(call, args.warmup)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_begin.record(stream)
-    for i in range(args.steps):
-        starts[i].record(stream)
-        call()
-        ends[i].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_begin.elapsed_time(t_end)
-    per_launch = [x.elapsed_time(y) for x, y in zip(starts, ends)]
-    ms_per_step = total_ms / args.steps
-    launch_ms = statistics.mean(per_launch)
+    sampler = SclkSampler()
+    warm = warm_up(call, args.warmup, sampler)
+    t = time_steps(call, args.steps, stream)
+    sclk = sampler.stop()
+    ms_per_step, launch_ms = t["ms_per_step"], t["launch_ms"]
     flops = 2.5 * w.flops(causal)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (launch_ms * 1e-3) / 1e12
@@ -475,10 +535,8 @@ def bench_backward(args, w, causal):
         "dtype": w.dtype,
         "data": "synthetic (seeded iid N(0,1) Q, K, V, dO)",
         "config": {"workload": w.name + "-backward", "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": causal,
-                   "scale": w.scale, "pct_of_mfma_peak": round(100 * value / MFMA_PEAK_TFLOPS, 2),
-                   "launch_ms_median": round(statistics.median(per_launch), 5),
-                   "launch_ms_min": round(min(per_launch), 5),
-                   "note": "one step = the dQ (with D) and dK/dV kernels of one attn_bwd call"},
+                   "scale": w.scale, "pct_of_mfma_peak": round(100 * value / MFMA_PEAK_TFLOPS, 2), **launch_stats(t),
+                   "sclk": sclk, "note": "one step = the dQ (with D) and dK/dV kernels of one attn_bwd call"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(w.name, causal, 0, BWD_SOURCE, key=f"{w.name}-causal{causal}-backward"),
@@ -513,23 +571,11 @@ def bench_merge(args, w, G):
     def call():
         eta.attn_lse_merge(o_parts, l_parts, o, lse, stream=stream)
 
-    warm = warm_up(call, args.warmup)
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_begin.record(stream)
-    for i in range(args.steps):
-        starts[i].record(stream)
-        call()
-        ends[i].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_begin.elapsed_time(t_end)
-    per_launch = [x.elapsed_time(y) for x, y in zip(starts, ends)]
-    ms_per_step = total_ms / args.steps
-    launch_ms = statistics.mean(per_launch)
+    sampler = SclkSampler()
+    warm = warm_up(call, args.warmup, sampler)
+    t = time_steps(call, args.steps, stream)
+    sclk = sampler.stop()
+    ms_per_step, launch_ms = t["ms_per_step"], t["launch_ms"]
     rows = w.B * w.H * w.N
     nbytes = G * rows * (w.d * 2 + 4) + rows * (w.d * 2 + 4)
     value = nbytes / (ms_per_step * 1e-3) / 1e9
@@ -540,8 +586,7 @@ def bench_merge(args, w, G):
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded shard results: O_g iid N(0,1), lse_g iid N(5,4))",
         "config": {"workload": f"{w.name}-merge{G}", "G": G, "rows": rows, "d": w.d,
-                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-                   "launch_ms_median": round(statistics.median(per_launch), 5)},
+                   "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2), **launch_stats(t), "sclk": sclk},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(w.name, None, 0, MERGE_SOURCE, key=f"{w.name}-merge{G}"),
@@ -670,26 +715,14 @@ def main():
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
-    warm = warm_up(lambda: eta.attn_fwd(q, k, v, out, lse, causal, w.scale, stream=stream, window=args.window),
-                   args.warmup)
-
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_begin.record(stream)
-    for i in range(args.steps):
-        starts[i].record(stream)
+    def call():
         eta.attn_fwd(q, k, v, out, lse, causal, w.scale, stream=stream, window=args.window)
-        ends[i].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
 
-    total_ms = t_begin.elapsed_time(t_end)
-    per_launch = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    ms_per_step = total_ms / args.steps
-    launch_ms = statistics.mean(per_launch)
+    sampler = SclkSampler()
+    warm = warm_up(call, args.warmup, sampler)
+    t = time_steps(call, args.steps, stream)
+    sclk = sampler.stop()
+    ms_per_step, launch_ms = t["ms_per_step"], t["launch_ms"]
     flops = launch_flops(w, causal, args.window)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (launch_ms * 1e-3) / 1e12
@@ -711,9 +744,9 @@ def main():
         "config": {"workload": w.name + (f"-window{args.window}" if args.window > 0 else ""),
                    "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": causal, "window": args.window,
                    "scale": w.scale, "layout": "[B,H,N,d] contiguous", "pct_of_mfma_peak": round(100 * value / MFMA_PEAK_TFLOPS, 2),
-                   "launch_ms_median": round(statistics.median(per_launch), 5),
-                   "launch_ms_p95": round(sorted(per_launch)[int(0.95 * (len(per_launch) - 1))], 5),
-                   "launch_ms_min": round(min(per_launch), 5)},
+                   **launch_stats(t), "sclk": sclk,
+                   "pct_of_peak_at_sclk": (round(100 * achieved / (MFMA_PEAK_TFLOPS * sclk["median_mhz"] / 2400.0), 2)
+                                           if sclk.get("median_mhz") else None)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(w.name, causal, args.window),

@@ -38,6 +38,7 @@
 #include <cstring>
 
 #include "attn_bwd.h"
+#include "launch.h"
 #include "lds_load.h"
 
 namespace {
@@ -52,11 +53,6 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-
-// the dQ kernel's MFMAs in fenced rounds with their LDS operands read a round ahead
-#ifndef ETA_BWD_DQ_ROUNDS
-#define ETA_BWD_DQ_ROUNDS 1
-#endif
 
 template <int DT> struct Elem;
 
@@ -325,7 +321,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 f32x16_t s[2], dp[2];
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb) s[sb] = dp[sb] = f32x16_t{};
-#if ETA_BWD_DQ_ROUNDS
                 {
                     // rounds of one S and one dP MFMA, the K and V rows of round
                     // r+1 read before round r's MFMAs (scheduling fences keep them there)
@@ -345,15 +340,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
-#else
-#pragma unroll
-                for (int ks = 0; ks < KSTEPS; ++ks)
-#pragma unroll
-                    for (int sb = 0; sb < 2; ++sb) {
-                        s[sb] = E::mfma(st.row(stg, 0, sb, ks), qf[ks], s[sb]);
-                        dp[sb] = E::mfma(st.row(stg, 1, sb, ks), df[ks], dp[sb]);
-                    }
-#endif
                 // dS^T = P^T (dP^T - D); register i of block sb is key kt0 + 32 sb + 16 (i/8) + 8 hf + i%8
                 const bool edge = (CAUSAL && kt0 + C::BT - 1 > qw0) || kt0 + C::BT > N;
                 const int hi = (CAUSAL ? min(qi, N - 1) : N - 1) - (kt0 + 8 * st.hf);
@@ -372,7 +358,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     dsf[kk] = u32x4_t{E::pack2(v[0], v[1]), E::pack2(v[2], v[3]), E::pack2(v[4], v[5]), E::pack2(v[6], v[7])};
                 }
                 // dQ^T += K^T dS^T
-#if ETA_BWD_DQ_ROUNDS
                 {
                     constexpr int R = 4 * DBLK;
                     u32x4_t to[2];
@@ -385,12 +370,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                         __builtin_amdgcn_sched_barrier(0);
                     }
                 }
-#else
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                    for (int db = 0; db < DBLK; ++db) acc[db] = E::mfma(st.tr(stg, 0, kk, db), dsf[kk], acc[db]);
-#endif
             }
             wait_loads();
             __syncthreads();
@@ -595,11 +574,10 @@ hipError_t launch(BwdArgs a, hipStream_t s) {
     const int ntile = (a.N + C::OWN - 1) / C::OWN;
     a.ntile = ntile;
     a.ngroups = CAUSAL ? (ntile + 1) / 2 : ntile;
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<D, DT, CAUSAL>), dim3((unsigned)a.ngroups * (unsigned)a.BH), dim3(C::NT), 0,
-                       s, a);
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<D, DT, CAUSAL>), dim3((unsigned)a.ngroups * (unsigned)a.BH), dim3(C::NT),
-                       0, s, a);
-    return hipGetLastError();
+    const dim3 grid((unsigned)a.ngroups * (unsigned)a.BH), block(C::NT);
+    const hipError_t e = launch_kernel(attn_bwd_dq_kernel<D, DT, CAUSAL>, grid, block, s, a);
+    if (e != hipSuccess) return e;
+    return launch_kernel(attn_bwd_dkdv_kernel<D, DT, CAUSAL>, grid, block, s, a);
 }
 
 template <int D, int DT>
@@ -635,12 +613,10 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
-}  // namespace
-
-extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* lse, const void* dout,
-                        void* dq, void* dk, void* dv, void* delta, int B, int H, int N, int d, int causal, float scale,
-                        int dtype, void* stream) {
-    if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !delta) return ATTN_ERR_NULL;
+// Host-side checks of everything but delta.
+int check_args(const void* q, const void* k, const void* v, const void* out, const void* lse, const void* dout,
+               void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale, int dtype) {
+    if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
     if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
     if (d != 64 && d != 80 && d != 128) return ATTN_ERR_HEAD_DIM;
     if (dtype != ATTN_F16 && dtype != ATTN_BF16) return ATTN_ERR_DTYPE;
@@ -652,21 +628,24 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out | (uintptr_t)dout | (uintptr_t)dq |
          (uintptr_t)dk | (uintptr_t)dv) & 15u)
         return ATTN_ERR_ALIGN;
-    if (((uintptr_t)lse | (uintptr_t)delta) & 3u) return ATTN_ERR_ALIGN;
+    if ((uintptr_t)lse & 3u) return ATTN_ERR_ALIGN;
     const size_t tb = (size_t)bh * (size_t)N * (size_t)d * 2u, rb = (size_t)bh * (size_t)N * 4u;
     const void* ins[6] = {q, k, v, out, dout, lse};
     const size_t insz[6] = {tb, tb, tb, tb, tb, rb};
-    void* outs[4] = {dq, dk, dv, delta};
-    const size_t outsz[4] = {tb, tb, tb, rb};
-    for (int i = 0; i < 4; ++i) {
+    void* outs[3] = {dq, dk, dv};
+    for (int i = 0; i < 3; ++i) {
         for (int j = 0; j < 6; ++j)
-            if (overlaps(outs[i], outsz[i], ins[j], insz[j])) return ATTN_ERR_ALIAS;
-        for (int j = i + 1; j < 4; ++j)
-            if (overlaps(outs[i], outsz[i], outs[j], outsz[j])) return ATTN_ERR_ALIAS;
+            if (overlaps(outs[i], tb, ins[j], insz[j])) return ATTN_ERR_ALIAS;
+        for (int j = i + 1; j < 3; ++j)
+            if (overlaps(outs[i], tb, outs[j], tb)) return ATTN_ERR_ALIAS;
     }
-    const int dev_status = check_device();
-    if (dev_status != ATTN_OK) return dev_status;
+    return ATTN_OK;
+}
 
+// Both kernels with D_i in `delta`; arguments already checked.
+int run(const void* q, const void* k, const void* v, const void* out, const void* lse, const void* dout, void* dq,
+        void* dk, void* dv, float* delta, int B, int H, int N, int d, int causal, float scale, int dtype,
+        void* stream) {
     BwdArgs a;
     a.q = static_cast<const u32x4_t*>(q);
     a.k = static_cast<const u32x4_t*>(k);
@@ -674,12 +653,12 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     a.o = static_cast<const u32x4_t*>(out);
     a.dout = static_cast<const u32x4_t*>(dout);
     a.lse = static_cast<const float*>(lse);
-    a.delta = static_cast<float*>(delta);
+    a.delta = delta;
     a.dq = static_cast<uint16_t*>(dq);
     a.dk = static_cast<uint16_t*>(dk);
     a.dv = static_cast<uint16_t*>(dv);
     a.N = N;
-    a.BH = (int)bh;
+    a.BH = B * H;
     a.ntile = 0;
     a.ngroups = 0;
     a.c = scale * kLog2e;
@@ -692,4 +671,24 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
         default: err = dispatch_dtype<128>(a, dtype, causal, s); break;
     }
     return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* out, const void* lse, const void* dout,
+                        void* dq, void* dk, void* dv, void* delta, int B, int H, int N, int d, int causal, float scale,
+                        int dtype, void* stream) {
+    if (!delta) return ATTN_ERR_NULL;
+    const int st = check_args(q, k, v, out, lse, dout, dq, dk, dv, B, H, N, d, causal, scale, dtype);
+    if (st != ATTN_OK) return st;
+    if ((uintptr_t)delta & 3u) return ATTN_ERR_ALIGN;
+    const long long bh = (long long)B * H;
+    const size_t tb = (size_t)bh * (size_t)N * (size_t)d * 2u, rb = (size_t)bh * (size_t)N * 4u;
+    const void* others[9] = {q, k, v, out, dout, dq, dk, dv, lse};
+    for (int j = 0; j < 9; ++j)
+        if (overlaps(delta, rb, others[j], j < 8 ? tb : rb)) return ATTN_ERR_ALIAS;
+    const int dev_status = check_device();
+    if (dev_status != ATTN_OK) return dev_status;
+    return run(q, k, v, out, lse, dout, dq, dk, dv, static_cast<float*>(delta), B, H, N, d, causal, scale, dtype,
+               stream);
 }

@@ -51,6 +51,7 @@
 #include <type_traits>
 
 #include "attn.h"
+#include "launch.h"
 #include "lds_load.h"
 
 namespace {
@@ -63,24 +64,11 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
-// the epilogue's O stores bypass L2 allocation (O is written once and not read back here)
-#ifndef ETA_FWD_NT_STORE
-#define ETA_FWD_NT_STORE 1
-#endif
-
-// Q rows (read once) are loaded with the non-temporal hint
-#ifndef ETA_FWD_NT_Q
-#define ETA_FWD_NT_Q 0
-#endif
-
-// log2 headroom before the reference max is raised (see Wave::prepare)
-#ifndef ETA_RESCALE_TH
-#define ETA_RESCALE_TH 8.0f
-#endif
-
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
+// log2 headroom before the reference max is raised (see Wave::prepare)
+constexpr float kRescaleTh = 8.0f;
 
 // --- element type ------------------------------------------------------------
 template <int DT> struct Elem;
@@ -279,30 +267,14 @@ struct Wave {
         }
     }
 
-    // start a query tile: this wave's rows begin at qw0_
-    // LOADQ false: the Q fragments come later from q_issue / q_read
-    template <bool LOADQ = true>
+    // start a query tile: this wave's rows begin at qw0_ (the Q fragments come
+    // later, from q_issue / q_read)
     __device__ __forceinline__ void begin(const FwdArgs& a, int bh, int qw0_) {
         qw0 = qw0_;
         qi = qw0 + n;
         const size_t hoff = (size_t)bh * (size_t)N * CPR;   // head offset in 16-byte chunks
         kbase = reinterpret_cast<const unsigned char*>(a.k + hoff);
         vbase = reinterpret_cast<const unsigned char*>(a.v + hoff);
-        if (!LOADQ) {
-        } else if (qi < N) {
-            const u32x4_t* src = a.q + hoff + (size_t)qi * CPR + hf;
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = src[2 * ks];
-            // only a negative scale flips Q's sign; with a positive one the loads
-            // are not waited for here and overlap the first K/V tile loads
-            if (a.qsign) {
-#pragma unroll
-                for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] ^= a.qsign;
-            }
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = u32x4_t{0, 0, 0, 0};
-        }
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) o[db] = f32x16_t{};
         m = kNegInf;
@@ -332,11 +304,7 @@ struct Wave {
 #pragma unroll
         for (int it = 0; it < 32 * C::CPRP / 64; ++it) {
             const int slot = it * 64 + lane, r = slot / C::CPRP, c = (slot % C::CPRP) ^ (r % C::CPRP);
-#if ETA_FWD_NT_Q
-            load_lds16_nt(desc, c < CPR ? (unsigned)(r * D * 2 + c * 16) : 0x80000000u, 0, slice + (unsigned)(it * 1024));
-#else
             load_lds16(desc, c < CPR ? (unsigned)(r * D * 2 + c * 16) : 0x80000000u, 0, slice + (unsigned)(it * 1024));
-#endif
         }
     }
 
@@ -377,28 +345,8 @@ struct Wave {
                 s[sb] = E::mfma(lds_read16(ka[ks] + ST * C::TILEB + sb * 32 * C::ROWB), qf[ks], s[sb]);
     }
 
-    // K fragments of the tile in stage ST (the score MFMAs' A operands), read
-    // ahead of the step that uses them
-    template <int ST>
-    __device__ __forceinline__ void kread(u32x4_t (&kf)[KSTEPS][SB]) const {
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks)
-#pragma unroll
-            for (int sb = 0; sb < SB; ++sb) kf[ks][sb] = lds_read16(ka[ks] + ST * C::TILEB + sb * 32 * C::ROWB);
-    }
-
-    // S^T = K Q^T from K fragments already in registers
-    __device__ __forceinline__ void score_reg(const u32x4_t (&kf)[KSTEPS][SB], f32x16_t (&s)[SB]) const {
-#pragma unroll
-        for (int sb = 0; sb < SB; ++sb) s[sb] = f32x16_t{};
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks)
-#pragma unroll
-            for (int sb = 0; sb < SB; ++sb) s[sb] = E::mfma(kf[ks][sb], qf[ks], s[sb]);
-    }
-
     // Mask tile j's scores where needed and update the reference max.  m is
-    // raised only when a tile's max exceeds it by more than ETA_RESCALE_TH (log2
+    // raised only when a tile's max exceeds it by more than kRescaleTh (log2
     // units), so p <= 2^TH and the O rescale is rare; m, l and O always refer to
     // the same m, so the result is unchanged.
     __device__ __forceinline__ void prepare(f32x16_t (&s)[SB], int j) {
@@ -426,7 +374,7 @@ struct Wave {
             for (int i = 0; i < 16; ++i) mc[i & 3] = fmaxf(mc[i & 3], s[sb][i]);
         const float mx = fmaxf(fmaxf(mc[0], mc[1]), fmaxf(mc[2], mc[3]));
         const float mt = pair_max(mx) * c;           // c > 0, so -inf stays -inf
-        const bool grow = mt > m + ETA_RESCALE_TH;
+        const bool grow = mt > m + kRescaleTh;
         if (__any(grow)) {
             const float mnew = grow ? mt : m;
             const float alpha = grow ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;   // 0 when m was -inf
@@ -470,52 +418,33 @@ struct Wave {
     }
 
     // The matrix half of a step: O^T += V^T P^T for the tile in V stage ST and
-    // S^T = K Q^T for the tile in K stage ST1, in rounds of up to RS MFMAs of
-    // each (one P.V and one score MFMA by default).  The LDS operands of round
-    // r+PD are read before round r's MFMAs (scheduling fences keep the compiler
-    // from sinking the reads next to their MFMAs), so PD+1 rounds of operands
-    // are live at a time.
-#ifndef ETA_FWD_PD
-#define ETA_FWD_PD 1
-#endif
-#ifndef ETA_FWD_RS
-#define ETA_FWD_RS 1
-#endif
+    // S^T = K Q^T for the tile in K stage ST1, in rounds of one P.V and one
+    // score MFMA.  The LDS operands of round r+1 are read before round r's
+    // MFMAs (scheduling fences keep the compiler from sinking the reads next to
+    // their MFMAs), so two rounds of operands are live at a time.
     template <int ST, int ST1>
     __device__ __forceinline__ void pv_score(const u32x4_t (&pf)[KK], f32x16_t (&s)[SB]) {
-        constexpr int NPV = KK * DBLK, NSC = KSTEPS * SB, RS = ETA_FWD_RS;
-        constexpr int R = ((NPV > NSC ? NPV : NSC) + RS - 1) / RS;
-        constexpr int PD = ETA_FWD_PD < R ? ETA_FWD_PD : R - 1, NB = PD + 1;
-        u32x4_t vo[NB][RS], ko[NB][RS];
+        constexpr int NPV = KK * DBLK, NSC = KSTEPS * SB;
+        constexpr int R = NPV > NSC ? NPV : NSC;
+        u32x4_t vo[2], ko[2];
         auto rd = [&](int r) {
-            const int b = r % NB;
-#pragma unroll
-            for (int i = 0; i < RS; ++i) {
-                const int pi = RS * r + i;
-                if (pi < NPV) {
-                    const int kk = pi / DBLK, db = pi % DBLK;
-                    const u32x2_t lo = lds_read_tr(va[db] + ST * C::TILEB + 16 * kk * C::ROWB);
-                    const u32x2_t hi = lds_read_tr(va[db] + ST * C::TILEB + (16 * kk + 4) * C::ROWB);
-                    vo[b][i] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-                }
-                if (pi < NSC) ko[b][i] = lds_read16(ka[pi / SB] + ST1 * C::TILEB + (pi % SB) * 32 * C::ROWB);
+            if (r < NPV) {
+                const int kk = r / DBLK, db = r % DBLK;
+                const u32x2_t lo = lds_read_tr(va[db] + ST * C::TILEB + 16 * kk * C::ROWB);
+                const u32x2_t hi = lds_read_tr(va[db] + ST * C::TILEB + (16 * kk + 4) * C::ROWB);
+                vo[r & 1] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
             }
+            if (r < NSC) ko[r & 1] = lds_read16(ka[r / SB] + ST1 * C::TILEB + (r % SB) * 32 * C::ROWB);
         };
 #pragma unroll
         for (int sb = 0; sb < SB; ++sb) s[sb] = f32x16_t{};
-#pragma unroll
-        for (int r = 0; r < PD; ++r) rd(r);
+        rd(0);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-            if (r + PD < R) rd(r + PD);
+            if (r + 1 < R) rd(r + 1);
             __builtin_amdgcn_sched_barrier(0);
-            const int b = r % NB;
-#pragma unroll
-            for (int i = 0; i < RS; ++i) {
-                const int pi = RS * r + i;
-                if (pi < NPV) o[pi % DBLK] = E::mfma(vo[b][i], pf[pi / DBLK], o[pi % DBLK]);
-                if (pi < NSC) s[pi % SB] = E::mfma(ko[b][i], qf[pi / SB], s[pi % SB]);
-            }
+            if (r < NPV) o[r % DBLK] = E::mfma(vo[r & 1], pf[r / DBLK], o[r % DBLK]);
+            if (r < NSC) s[r % SB] = E::mfma(ko[r & 1], qf[r / SB], s[r % SB]);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -565,12 +494,8 @@ struct Wave {
         for (int k = 0; k < 32 / RPR; ++k) {
             const int r = k * RPR + rr;
             if (c < CPR && qw0 + r < N) {
-                u32x4_t* dst = reinterpret_cast<u32x4_t*>(obase + (unsigned)(r * D + 8 * c));
-#if ETA_FWD_NT_STORE
-                __builtin_nontemporal_store(v[k], dst);
-#else
-                *dst = v[k];
-#endif
+                // O is written once and not read back here: the stores bypass L2 allocation
+                __builtin_nontemporal_store(v[k], reinterpret_cast<u32x4_t*>(obase + (unsigned)(r * D + 8 * c)));
             }
         }
         if (a.lse != nullptr && hf == 0 && qi < N) a.lse[(size_t)bh * N + qi] = (m + __builtin_amdgcn_logf(ltot)) * kLn2;
@@ -579,39 +504,21 @@ struct Wave {
 
 #endif  // __HIP_DEVICE_COMPILE__
 
-// ---- the kernel: WAVES free-running waves per work-group ---------------------
-// The 8-wave schedule without a window runs a three-stage K/V ring: the
-// barrier of step j sits between its score MFMAs and its softmax.  It makes
-// tile j+1 visible (its loads were issued a step earlier) and frees the stage
-// of tile j-1 (every wave has finished that tile's P.V), which then receives
-// tile j+2.  Right after it the wave reads tile j+1's K fragments, so the next
-// step's score MFMAs start from registers with no barrier or LDS wait in front
-// of them.
-#ifndef ETA_FWD_RING
-#define ETA_FWD_RING 1
-#endif
-// The 8-wave schedule with two wave groups in alternation (see the kernel).
-#ifndef ETA_FWD_PING
-#define ETA_FWD_PING 1
-#endif
-// the two-group kernel's first wait of a query tile covers only Q and tile 0's K
-#ifndef ETA_FWD_PWAIT
-#define ETA_FWD_PWAIT 1
-#endif
-template <int WAVES, bool WIN> constexpr bool fwd_ping() { return ETA_FWD_PING && WAVES == 8; }
-template <int WAVES, bool WIN> constexpr int fwd_stages() {
-    return fwd_ping<WAVES, WIN>() || (ETA_FWD_RING && WAVES == 8 && !WIN) ? 3 : 2;
-}
+// ---- the kernel ---------------------------------------------------------------
+// 4 waves: free-running waves, two K/V stages.  8 waves: two wave groups in
+// alternation over a three-stage K/V ring (see the kernel).
+template <int WAVES> constexpr bool fwd_ping() { return WAVES == 8; }
+template <int WAVES> constexpr int fwd_stages() { return fwd_ping<WAVES>() ? 3 : 2; }
 
 template <int D, int DT, bool CAUSAL, int WAVES, bool WIN>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
-    constexpr int STAGES = fwd_stages<WAVES, WIN>();
+    constexpr int STAGES = fwd_stages<WAVES>();
     using C = Cfg<D, WAVES, STAGES>;
     // the two-group schedule adds room for the Q slices of waves 4-7 (waves 0-3
     // use the K and V areas of stage 2, free while a query tile's loads start)
-    constexpr int QEXTRA = fwd_ping<WAVES, WIN>() ? 4 * 32 * C::ROWB : 0;
+    constexpr int QEXTRA = fwd_ping<WAVES>() ? 4 * 32 * C::ROWB : 0;
     static_assert(C::LDS + QEXTRA <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS + QEXTRA];
     const int tid = threadIdx.x;
@@ -631,10 +538,8 @@ void attn_fwd_kernel(FwdArgs a) {
     for (int item = 0; item < nitems; ++item, first = false) {
         const int qt = CAUSAL ? (item == 0 ? a.nqt - 1 - grp : grp) : grp;
         const int q0 = qt * C::BM;
-        // Q rows through LDS (q_issue / q_read) in the two-group kernel and in the
-        // 4-wave two-stage one (whose stage 1 is free until the first step)
-        constexpr bool QLDS = fwd_ping<WAVES, WIN>() || (STAGES == 2 && WAVES == 4);
-        w.template begin<!QLDS>(a, bh, q0 + 32 * wave);
+        // Q rows come through LDS (q_issue / q_read) in both schedules
+        w.begin(a, bh, q0 + 32 * wave);
         // key tiles jlo .. nt-1: up to the last query (causal) or its band's end,
         // from the first query's band start
         const int win = WIN ? a.window : 0;
@@ -642,7 +547,7 @@ void attn_fwd_kernel(FwdArgs a) {
         const int nt = (kend + C::BN - 1) / C::BN;
         const int jlo = win > 0 ? max(0, q0 - win + 1) / C::BN : 0;
 
-        if constexpr (fwd_ping<WAVES, WIN>()) {
+        if constexpr (fwd_ping<WAVES>()) {
             // Two groups of four waves, one wave of each on every SIMD.  Every
             // wave runs the same sequence per key tile u (u = 0 .. T-1 from jlo):
             //     Y(u)  barrier  X(u)  barrier
@@ -713,22 +618,16 @@ void attn_fwd_kernel(FwdArgs a) {
                 w.issue(false, jlo + 1, 1);
                 w.issue(true, jlo + 1, 1);
             }
-#if ETA_FWD_PWAIT
             // only Q and tile 0's K are needed for the first scores: tile 0's V and
             // tile 1 (issued after them) are waited for before the barrier that
             // ends slot 0 (group 0 in its first tile step, group 1 just below)
             if (T > 1) wait_vmcnt<3 * C::IT>();
             else wait_vmcnt<C::IT>();
-#else
-            wait_loads();
-#endif
             w.q_read(a, qslice);                           // this wave's own loads: no barrier needed
             __syncthreads();
             if (w.active(jlo)) w.template score<0>(s);
             if (!g0) {
-#if ETA_FWD_PWAIT
                 wait_loads();
-#endif
                 __syncthreads();
             }
             for (int u = 0; u < T; u += 3) {
@@ -737,48 +636,6 @@ void attn_fwd_kernel(FwdArgs a) {
                 if (u + 2 < T) tile(std::integral_constant<int, 2>{}, u + 2);
             }
             if (g0) __syncthreads();
-            w.finish(a, bh);
-            continue;
-        } else if constexpr (STAGES == 3) {
-            if (!first) __syncthreads();                   // every wave has left the previous item's tiles
-            u32x4_t kf[C::KSTEPS][C::SB];
-            auto rstep = [&](auto stage_tag, int j) {
-                constexpr int ST = decltype(stage_tag)::value, ST1 = (ST + 1) % 3, ST2 = (ST + 2) % 3;
-                const bool act = w.active(j);
-                f32x16_t s[C::SB];
-                if (act) {
-                    __builtin_amdgcn_s_setprio(2);
-                    w.score_reg(kf, s);
-                    __builtin_amdgcn_s_setprio(0);
-                }
-                wait_loads();                               // this wave's share of tile j+1
-                __syncthreads();                            // tile j+1 visible, tile j-1's stage free
-                if (j + 2 < nt) {
-                    w.issue(false, j + 2, ST2);
-                    w.issue(true, j + 2, ST2);
-                }
-                if (j + 1 < nt && w.active(j + 1)) w.template kread<ST1>(kf);
-                if (act) {
-                    u32x4_t pf[C::KK];
-                    w.prepare(s, j);
-                    w.probs(s, pf);
-                    w.template pv<ST>(pf);
-                }
-            };
-            w.issue(false, jlo, 0);
-            w.issue(true, jlo, 0);
-            if (jlo + 1 < nt) {
-                w.issue(false, jlo + 1, 1);
-                w.issue(true, jlo + 1, 1);
-            }
-            wait_loads();
-            __syncthreads();
-            if (w.active(jlo)) w.template kread<0>(kf);
-            for (int j = jlo; j < nt; j += 3) {             // tile j in stage (j - jlo) % 3
-                rstep(std::integral_constant<int, 0>{}, j);
-                if (j + 1 < nt) rstep(std::integral_constant<int, 1>{}, j + 1);
-                if (j + 2 < nt) rstep(std::integral_constant<int, 2>{}, j + 2);
-            }
             w.finish(a, bh);
             continue;
         }
@@ -812,14 +669,11 @@ void attn_fwd_kernel(FwdArgs a) {
         const unsigned qslice = (unsigned)(size_t)(lds_bytes)smem +
                                 (unsigned)(wave < 2 ? C::KOFF + C::TILEB + wave * 32 * C::ROWB
                                                     : C::VOFF + C::TILEB + (wave - 2) * 32 * C::ROWB);
-        constexpr bool QLDS2 = STAGES == 2 && WAVES == 4;    // four Q slices fill stage 1
-        if constexpr (QLDS2) {
-            if (w.qw0 < a.N) w.q_issue(a, bh, qslice);
-        }
+        if (w.qw0 < a.N) w.q_issue(a, bh, qslice);           // four Q slices fill stage 1
         w.issue(false, jlo, 0);
         w.issue(true, jlo, 0);
         wait_loads();
-        if constexpr (QLDS2) w.q_read(a, qslice);        // this wave's own loads: no barrier needed
+        w.q_read(a, qslice);                               // this wave's own loads: no barrier needed
         __syncthreads();
         for (int j = jlo; j < nt; j += 2) {                 // tile j in stage (j - jlo) & 1
             step(std::integral_constant<int, 0>{}, j);
@@ -836,10 +690,7 @@ void attn_fwd_kernel(FwdArgs a) {
 // Work-groups of 256 queries needed before the 8-wave kernel is used: below
 // about two rounds of the 256 CUs (one such work-group fits per CU) the
 // 128-query work-groups fill the chip better.
-#ifndef ETA_WIDE_MIN_GROUPS
-#define ETA_WIDE_MIN_GROUPS 512
-#endif
-constexpr long long kWideMinGroups = ETA_WIDE_MIN_GROUPS;
+constexpr long long kWideMinGroups = 512;
 
 bool use_wide(long long bh, long long N, int causal) {
     const long long nqt = (N + 255) / 256;
@@ -849,9 +700,6 @@ bool use_wide(long long bh, long long N, int causal) {
 // Resident work-groups for the 8-wave schedule: one per CU (its LDS stages
 // leave room for no second one), each looping over work units, so that the
 // grid runs as one round instead of several.
-#ifndef ETA_FWD_PERSIST
-#define ETA_FWD_PERSIST 1
-#endif
 
 template <int D, int DT, bool CAUSAL, int WAVES, bool WIN>
 hipError_t launch_waves(FwdArgs a, hipStream_t stream, int cus) {
@@ -861,9 +709,8 @@ hipError_t launch_waves(FwdArgs a, hipStream_t stream, int cus) {
     a.ngroups = CAUSAL ? (int)((nqt + 1) / 2) : (int)nqt;
     const unsigned units = (unsigned)a.ngroups * (unsigned)a.BH;
     unsigned grid = units;
-    if (ETA_FWD_PERSIST && fwd_ping<WAVES, WIN>() && cus >= 8 && units > (unsigned)cus) grid = (unsigned)cus & ~7u;
-    hipLaunchKernelGGL((attn_fwd_kernel<D, DT, CAUSAL, WAVES, WIN>), dim3(grid), dim3(64 * WAVES), 0, stream, a);
-    return hipGetLastError();
+    if (fwd_ping<WAVES>() && cus >= 8 && units > (unsigned)cus) grid = (unsigned)cus & ~7u;
+    return launch_kernel(attn_fwd_kernel<D, DT, CAUSAL, WAVES, WIN>, dim3(grid), dim3(64 * WAVES), stream, a);
 }
 
 template <int D, int DT, bool CAUSAL>

@@ -41,6 +41,7 @@
 #include <cstring>
 
 #include "gemm.h"
+#include "launch.h"
 #include "lds_load.h"
 
 namespace {
@@ -102,22 +103,7 @@ template <> struct Elem<ATTN_BF16> {
 // BK rows (k) of BN values of n (512 bytes); its 64-byte granule g of row r
 // sits at g ^ (r % 8), so the transpose reads of 16 lanes (4 rows x 4 granule
 // offsets) spread over the banks.
-// C rows are stored with the non-temporal hint (written once, not read back)
-// the two-group kernel (below) and whether it spreads each tile's load rounds
-// over its phases instead of issuing them at a phase's start
-#ifndef ETA_GEMM_PP
-#define ETA_GEMM_PP 1
-#endif
-#ifndef ETA_GEMM_SPREAD
-#define ETA_GEMM_SPREAD 1
-#endif
-
-#ifndef ETA_GEMM_NT_STORE
-#define ETA_GEMM_NT_STORE 1
-#endif
-#ifndef ETA_GEMM_GROUP_M
-#define ETA_GEMM_GROUP_M 4
-#endif
+// C rows are stored with the non-temporal hint (written once, not read back).
 
 // WAVES waves per work-group in a WAVES_N (along n) x WAVES / WAVES_N (along m)
 // grid; K in steps of BK (64 or 32) through STAGES LDS stages
@@ -138,7 +124,7 @@ struct Cfg {
     static constexpr int LDS = STAGES * STAGE;
     static constexpr int ROUNDS = BM * ROWB / (16 * NT);   // direct-load rounds per tile (A and B alike)
     static constexpr int LOADS = 2 * ROUNDS;               // direct loads per tile and wave
-    static constexpr int GROUP_M = ETA_GEMM_GROUP_M; // tile rows per group of the launch order
+    static constexpr int GROUP_M = 4;                // tile rows per group of the launch order
     static_assert(BK == 32 || BK == 64, "k step");
     static_assert(BN * BK * 2 == BM * ROWB, "both tiles take the same number of load rounds");
     static_assert(WAVES % WAVES_N == 0 && WM % 32 == 0 && WN % 32 == 0, "wave layouts");
@@ -367,30 +353,13 @@ struct Tile {
         for (int mb = 0; mb < C::MB; ++mb) bv[mb] = lds_read16(base + ra + ch + mb * 32 * C::ROWB);
     }
 
-    // the tile in the stage at byte offset `stage`: KS k-steps of NB x MB MFMAs,
-    // the operands of step s+1 read while the MFMAs of step s run
-    __device__ __forceinline__ void compute(unsigned stage) {
-        const unsigned base = lds0 + stage;
-        u32x4_t av[2][C::NB], bv[2][C::MB];
-        operands(base, 0, av[0], bv[0]);
-#pragma unroll
-        for (int s = 0; s < C::KS; ++s) {
-            if (s + 1 < C::KS) operands(base, s + 1, av[(s + 1) & 1], bv[(s + 1) & 1]);
-#pragma unroll
-            for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-                for (int mb = 0; mb < C::MB; ++mb) acc[nb][mb] = E::mfma(av[s & 1][nb], bv[s & 1][mb], acc[nb][mb]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-
     // every operand of the tile in the stage at byte offset `stage`, all KS k-steps;
     // with j >= 0, tile j's load rounds are issued in between (LOADS / KS per k-step)
     __device__ __forceinline__ void load_step(const GemmArgs& g, unsigned stage, u32x4_t (&av)[C::KS][C::NB],
                                               u32x4_t (&bv)[C::KS][C::MB], int j, unsigned jstage) const {
 #pragma unroll
         for (int s = 0; s < C::KS; ++s) {
-            if (ETA_GEMM_SPREAD && j >= 0) issue_rounds(g, j, jstage, s * C::LOADS / C::KS, (s + 1) * C::LOADS / C::KS);
+            if (j >= 0) issue_rounds(g, j, jstage, s * C::LOADS / C::KS, (s + 1) * C::LOADS / C::KS);
             operands(lds0 + stage, s, av[s], bv[s]);
         }
     }
@@ -405,7 +374,7 @@ struct Tile {
             for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
                 for (int mb = 0; mb < C::MB; ++mb) acc[nb][mb] = E::mfma(av[s][nb], bv[s][mb], acc[nb][mb]);
-            if (ETA_GEMM_SPREAD && j >= 0) issue_rounds(g, j, jstage, s * C::LOADS / C::KS, (s + 1) * C::LOADS / C::KS);
+            if (j >= 0) issue_rounds(g, j, jstage, s * C::LOADS / C::KS, (s + 1) * C::LOADS / C::KS);
         }
     }
 
@@ -472,11 +441,7 @@ struct Tile {
             if (m >= g.M || n >= g.N) continue;
             unsigned char* dst = g.c + (size_t)m * (size_t)g.ldc + (size_t)n * 2;
             if (n + 7 < g.N) {
-#if ETA_GEMM_NT_STORE
                 __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(dst));
-#else
-                *reinterpret_cast<u32x4_t*>(dst) = v;
-#endif
             } else {
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
@@ -518,43 +483,6 @@ struct Tile {
 
 #endif  // __HIP_DEVICE_COMPILE__
 
-
-template <int DT, bool BKN, int WAVES, int WAVES_N, int BK, int STAGES>
-__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4)))
-void gemm_kernel(GemmArgs g) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    using C = Cfg<WAVES, WAVES_N, BK, STAGES>;
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[C::LDS];
-    Tile<DT, BKN, C> t;
-    int tile_m, tile_n;
-    map_tile(g, tile_m, tile_n);
-    t.init(g, (unsigned)(size_t)(lds_bytes)lds, tile_m, tile_n);
-    const int nk = (g.K + C::BK - 1) / C::BK;
-    // tiles 0 .. STAGES-2 in flight before the loop; step j waits for tile j
-    // (the loads of up to STAGES-2 later tiles may stay outstanding), then every
-    // wave has left step j-1, so tile j+STAGES-1 may refill that step's stage
-#pragma unroll
-    for (int p = 0; p < STAGES - 1; ++p)
-        if (p < nk) t.issue(g, p, p * C::STAGE);
-    for (int j = 0; j < nk; ++j) {
-        const int later = min(STAGES - 2, nk - 1 - j);   // tiles issued after tile j, still loading
-        if constexpr (STAGES >= 4) {
-            if (later >= 2) wait_vmcnt<2 * C::LOADS>();
-            else if (later == 1) wait_vmcnt<C::LOADS>();
-            else wait_vmcnt<0>();
-        } else if constexpr (STAGES == 3) {
-            if (later >= 1) wait_vmcnt<C::LOADS>();
-            else wait_vmcnt<0>();
-        } else {
-            wait_vmcnt<0>();
-        }
-        __syncthreads();
-        if (j + STAGES - 1 < nk) t.issue(g, j + STAGES - 1, ((j + STAGES - 1) % STAGES) * C::STAGE);
-        t.compute((j % STAGES) * C::STAGE);
-    }
-    t.finish(g);
-#endif
-}
 
 // Two wave groups in alternation (8 waves, 2 LDS stages): waves 0-3 and 4-7,
 // one of each on every SIMD, run the same sequence per k tile i,
@@ -598,11 +526,9 @@ void gemm_kernel_pp(GemmArgs g) {
         const unsigned st = (unsigned)(i & 1) * C::STAGE;
         const int j0 = g0 && i + 1 < nk ? i + 1 : -1;   // group 0: tile i+1 during M(i)
         const int j1 = !g0 && i + 2 < nk ? i + 2 : -1;  // group 1: tile i+2 during X(i)
-        if (!ETA_GEMM_SPREAD && j0 >= 0) t.issue(g, j0, C::STAGE - st);
         t.load_step(g, st, av, bv, j0, C::STAGE - st);
         if (!g0) wait_vmcnt<0>();                    // slot 2i+1 ends (group 1): tile i+1 landed
         __syncthreads();
-        if (!ETA_GEMM_SPREAD && j1 >= 0) t.issue(g, j1, st);   // slot 2i+2 starts (group 1)
         __builtin_amdgcn_s_setprio(2);
         t.mma_step(g, av, bv, j1, st);
         __builtin_amdgcn_s_setprio(0);
@@ -636,43 +562,17 @@ int check_device() {
 
 bool overlaps(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) { return a0 < b1 && b0 < a1; }
 
-// the launched configuration: waves per work-group, how many of them split n,
-// the k step and the number of LDS stages
-#ifndef ETA_GEMM_WAVES
-#define ETA_GEMM_WAVES 8
-#endif
-#ifndef ETA_GEMM_WAVES_N
-#define ETA_GEMM_WAVES_N 2
-#endif
-#ifndef ETA_GEMM_BK
-#define ETA_GEMM_BK 64
-#endif
-#ifndef ETA_GEMM_STAGES
-#define ETA_GEMM_STAGES 2
-#endif
+// The launched configuration: 8 waves (two groups of four, see gemm_kernel_pp),
+// two of them along n, k steps of 64 through two LDS stages.
+using Launch = Cfg<8, 2, 64, 2>;
 
-
-template <int WAVES, int WAVES_N, int BK, int STAGES>
 hipError_t launch(const GemmArgs& g, int dtype, bool bkn, hipStream_t s) {
-    const dim3 grid((unsigned)(g.tm * g.tn)), block(64 * WAVES);
-    if constexpr (ETA_GEMM_PP && WAVES == 8 && STAGES == 2) {
-        if (dtype == ATTN_BF16) {
-            if (bkn) hipLaunchKernelGGL((gemm_kernel_pp<ATTN_BF16, true, WAVES, WAVES_N, BK, STAGES>), grid, block, 0, s, g);
-            else hipLaunchKernelGGL((gemm_kernel_pp<ATTN_BF16, false, WAVES, WAVES_N, BK, STAGES>), grid, block, 0, s, g);
-        } else {
-            if (bkn) hipLaunchKernelGGL((gemm_kernel_pp<ATTN_F16, true, WAVES, WAVES_N, BK, STAGES>), grid, block, 0, s, g);
-            else hipLaunchKernelGGL((gemm_kernel_pp<ATTN_F16, false, WAVES, WAVES_N, BK, STAGES>), grid, block, 0, s, g);
-        }
-        return hipGetLastError();
-    }
-    if (dtype == ATTN_BF16) {
-        if (bkn) hipLaunchKernelGGL((gemm_kernel<ATTN_BF16, true, WAVES, WAVES_N, BK, STAGES>), grid, block, 0, s, g);
-        else hipLaunchKernelGGL((gemm_kernel<ATTN_BF16, false, WAVES, WAVES_N, BK, STAGES>), grid, block, 0, s, g);
-    } else {
-        if (bkn) hipLaunchKernelGGL((gemm_kernel<ATTN_F16, true, WAVES, WAVES_N, BK, STAGES>), grid, block, 0, s, g);
-        else hipLaunchKernelGGL((gemm_kernel<ATTN_F16, false, WAVES, WAVES_N, BK, STAGES>), grid, block, 0, s, g);
-    }
-    return hipGetLastError();
+    const dim3 grid((unsigned)(g.tm * g.tn)), block(Launch::NT);
+    if (dtype == ATTN_BF16)
+        return bkn ? launch_kernel(gemm_kernel_pp<ATTN_BF16, true, 8, 2, 64, 2>, grid, block, s, g)
+                   : launch_kernel(gemm_kernel_pp<ATTN_BF16, false, 8, 2, 64, 2>, grid, block, s, g);
+    return bkn ? launch_kernel(gemm_kernel_pp<ATTN_F16, true, 8, 2, 64, 2>, grid, block, s, g)
+               : launch_kernel(gemm_kernel_pp<ATTN_F16, false, 8, 2, 64, 2>, grid, block, s, g);
 }
 
 }  // namespace
@@ -725,6 +625,5 @@ extern "C" int gemm_bias_act(const void* a, long long lda, const void* b, long l
     g.tn = (int)tn;
     g.c_vec = ((uintptr_t)c % 8 == 0) && (ldc % 4 == 0);
     g.c_vec16 = ((uintptr_t)c % 16 == 0) && (ldc % 8 == 0);
-    return launch<ETA_GEMM_WAVES, ETA_GEMM_WAVES_N, ETA_GEMM_BK, ETA_GEMM_STAGES>(g, dtype, bkn,
-                                                                                 static_cast<hipStream_t>(stream)) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+    return launch(g, dtype, bkn, static_cast<hipStream_t>(stream)) == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }

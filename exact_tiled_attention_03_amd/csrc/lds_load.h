@@ -4,6 +4,11 @@
 // lds_dst + size * i (lds_dst wave-uniform, passed through M0).  Offsets at or
 // past the descriptor's size read as zero.
 //
+// M0 carries the LDS destination.  gfx950 needs one wait state between an SALU
+// write of M0 and an LDS-DMA load that reads it; the compiler inserts it for its
+// own loads but cannot see inside inline assembly, so each sequence below
+// carries its own s_nop 0.
+//
 // Written as inline assembly: when the compiler sees these loads as builtins it
 // treats them as pending LDS stores, so it makes every later LDS transpose read
 // and every work-group barrier wait for all of them (including prefetches of
@@ -30,21 +35,13 @@ __device__ __forceinline__ eta_desc_t buffer_desc(const void* base, int bytes) {
 }
 
 __device__ __forceinline__ void load_lds16(const eta_desc_t& desc, unsigned voff, unsigned soff, unsigned lds_dst) {
-    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(desc),
-                 "s"(__builtin_amdgcn_readfirstlane(soff)), "s"(__builtin_amdgcn_readfirstlane(lds_dst))
-                 : "memory");
-}
-
-// the same for data read once (the non-temporal hint keeps it from displacing
-// lines that other work-groups will read again)
-__device__ __forceinline__ void load_lds16_nt(const eta_desc_t& desc, unsigned voff, unsigned soff, unsigned lds_dst) {
-    asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen nt lds" ::"v"(voff), "s"(desc),
+    asm volatile("s_mov_b32 m0, %3\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(desc),
                  "s"(__builtin_amdgcn_readfirstlane(soff)), "s"(__builtin_amdgcn_readfirstlane(lds_dst))
                  : "memory");
 }
 
 __device__ __forceinline__ void load_lds4(const eta_desc_t& desc, unsigned voff, unsigned lds_dst) {
-    asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(desc),
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(desc),
                  "s"(__builtin_amdgcn_readfirstlane(lds_dst))
                  : "memory");
 }

@@ -18,15 +18,7 @@
 #include <cstring>
 
 #include "attn_bwd.h"
-
-// Shards whose loads are issued together, and whether the parts (read once) and
-// the result (written once) bypass the caches.
-#ifndef ETA_MERGE_UNROLL
-#define ETA_MERGE_UNROLL 8
-#endif
-#ifndef ETA_MERGE_STREAM
-#define ETA_MERGE_STREAM 1
-#endif
+#include "launch.h"
 
 namespace {
 
@@ -80,7 +72,8 @@ template <int DT>
 __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using T = Ty<DT>;
-    constexpr int U = ETA_MERGE_UNROLL;
+    constexpr int U = 8;   // shards whose loads are issued together
+    // the parts (read once) and the result (written once) bypass the caches
     const int sub = threadIdx.x & 15;
     const bool own = sub < a.CPR;
     const long long stride = (long long)gridDim.x * 16;
@@ -96,7 +89,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
                 lg[u] = g < a.G ? a.lse_parts[(long long)g * a.R + r] : kNegInf;
                 const u32x4_t* src = a.o_parts + ((long long)g * a.R + r) * a.CPR + sub;
                 v[u] = u32x4_t{0, 0, 0, 0};
-                if (g < a.G && own) v[u] = ETA_MERGE_STREAM ? __builtin_nontemporal_load(src) : *src;
+                if (g < a.G && own) v[u] = __builtin_nontemporal_load(src);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -120,10 +113,7 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(MergeArgs a) {
         const float inv = tot > 0.f ? 1.0f / tot : 0.f;
         const u32x4_t res{T::pack2(acc[0] * inv, acc[1] * inv), T::pack2(acc[2] * inv, acc[3] * inv),
                           T::pack2(acc[4] * inv, acc[5] * inv), T::pack2(acc[6] * inv, acc[7] * inv)};
-        if (own) {
-            if (ETA_MERGE_STREAM) __builtin_nontemporal_store(res, a.o + r * a.CPR + sub);
-            else a.o[r * a.CPR + sub] = res;
-        }
+        if (own) __builtin_nontemporal_store(res, a.o + r * a.CPR + sub);
         if (sub == 0) a.lse[r] = m > kNegInf ? m + __builtin_amdgcn_logf(tot) * kLn2 : kNegInf;
     }
 #endif
@@ -178,7 +168,7 @@ extern "C" int attn_lse_merge(const void* o_parts, const void* lse_parts, int G,
     const long long groups = (R + 15) / 16;
     const dim3 grid((unsigned)(groups < 65536 ? groups : 65536)), block(256);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (dtype == ATTN_BF16) hipLaunchKernelGGL((lse_merge_kernel<ATTN_BF16>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((lse_merge_kernel<ATTN_F16>), grid, block, 0, s, a);
-    return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+    const hipError_t e = dtype == ATTN_BF16 ? launch_kernel(lse_merge_kernel<ATTN_BF16>, grid, block, s, a)
+                                            : launch_kernel(lse_merge_kernel<ATTN_F16>, grid, block, s, a);
+    return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }

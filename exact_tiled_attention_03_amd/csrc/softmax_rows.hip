@@ -24,6 +24,7 @@
 #include <cstdint>
 #include <cstring>
 
+#include "launch.h"
 #include "softmax.h"
 
 namespace {
@@ -311,8 +312,7 @@ unsigned grid_for(long long rows) { return (unsigned)(rows < kMaxGroups ? rows :
 
 template <int DT, bool WIDE, int NT, int ITEMS>
 hipError_t launch_row(const SmArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL((softmax_row_kernel<DT, WIDE, NT, ITEMS>), dim3(grid_for(a.rows)), dim3(NT), 0, s, a);
-    return hipGetLastError();
+    return launch_kernel(softmax_row_kernel<DT, WIDE, NT, ITEMS>, dim3(grid_for(a.rows)), dim3(NT), s, a);
 }
 
 template <int DT, bool WIDE, int NT>
@@ -357,8 +357,7 @@ hipError_t dispatch(const SmArgs& a, hipStream_t s) {
     if (nu <= 512LL * IMAX) return launch_items<DT, WIDE, 512>(a, pow2_at_least((nu + 511) / 512), s);
     if (nu <= 1024LL * IMAX) return launch_items<DT, WIDE, 1024>(a, pow2_at_least((nu + 1023) / 1024), s);
     constexpr int TI = WIDE ? 4 : 16;   // 16-byte vectors: 4 per tile; elements: 16 per tile
-    hipLaunchKernelGGL((softmax_row_tiled_kernel<DT, WIDE, 1024, TI>), dim3(grid_for(a.rows)), dim3(1024), 0, s, a);
-    return hipGetLastError();
+    return launch_kernel(softmax_row_tiled_kernel<DT, WIDE, 1024, TI>, dim3(grid_for(a.rows)), dim3(1024), s, a);
 }
 
 template <int DT>
