@@ -56,6 +56,9 @@ def load_library():
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int,
                                                                            ctypes.c_void_p]
+    lib.attn_bwd_noalloc.restype = ctypes.c_int
+    lib.attn_bwd_noalloc.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int,
+                                                                                 ctypes.c_void_p]
     lib.attn_lse_merge.restype = ctypes.c_int
     lib.attn_lse_merge.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
@@ -220,6 +223,34 @@ def attn_bwd(q, k, v, out, lse, dout, dq=None, dk=None, dv=None, delta=None, cau
     if st != ATTN_OK:
         raise AttnError(st, attn_status_string(st))
     return dq, dk, dv, delta
+
+
+def attn_bwd_noalloc(q, k, v, out, lse, dout, dq, dk, dv, causal=True, scale=None, stream=None):
+    """attn_bwd_noalloc: the gradients of attn_bwd into the given dq, dk, dv, with D_i
+    kept in the library's own per-GPU device array (nothing is allocated, here or in
+    the library; B*H*N must not exceed ATTN_BWD_NOALLOC_MAX_ROWS).  Tensors as for
+    attn_bwd.  Returns (dq, dk, dv)."""
+    import math
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    for name, t in (("k", k), ("v", v), ("out", out), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        if tuple(t.shape) != (B, H, N, d) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be [B, H, N, d] of {q.dtype}")
+    if tuple(lse.shape) != (B, H, N) or str(lse.dtype) != "torch.float32":
+        raise ValueError("lse must be float32 [B, H, N]")
+    for t in (q, k, v, out, lse, dout, dq, dk, dv):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous GPU tensors")
+    st = lib.attn_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                              dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d,
+                              int(bool(causal)), float(scale), _dtype_code(q), _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, attn_status_string(st))
+    return dq, dk, dv
 
 
 def attn_lse_merge(o_parts, lse_parts, o=None, lse=None, stream=None):

@@ -36,6 +36,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "attn_bwd.h"
 #include "launch.h"
@@ -613,7 +614,31 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
-// Host-side checks of everything but delta.
+// Device scratch of attn_bwd_noalloc: D_i of up to kNoallocRows rows.  One copy
+// per GPU (each device that loads the library holds its own, until the process
+// ends); host code reaches it only through the address hipGetSymbolAddress
+// returns for the current device, never through the array's name.
+constexpr long long kNoallocRows = ATTN_BWD_NOALLOC_MAX_ROWS;
+static __device__ __align__(256) float scratch[kNoallocRows];
+
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices];   // per device, under g_scratch_mu
+
+// The current device's scratch address, looked up once per device (with that
+// device current) and kept; nullptr if the lookup fails.
+float* device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+        g_scratch_ptr[dev] = static_cast<float*>(p);
+    }
+    return g_scratch_ptr[dev];
+}
+
+// Host-side checks shared by both entry points (delta is checked by attn_bwd).
 int check_args(const void* q, const void* k, const void* v, const void* out, const void* lse, const void* dout,
                void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal, float scale, int dtype) {
     if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return ATTN_ERR_NULL;
@@ -691,4 +716,20 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
     if (dev_status != ATTN_OK) return dev_status;
     return run(q, k, v, out, lse, dout, dq, dk, dv, static_cast<float*>(delta), B, H, N, d, causal, scale, dtype,
                stream);
+}
+
+extern "C" int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* out, const void* lse,
+                                const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal,
+                                float scale, int dtype, void* stream) {
+    // sizes past the array are refused first, before the checks that derive spans from them
+    if (B >= 1 && H >= 1 && N >= 1 && (long long)B * H * N > kNoallocRows) return ATTN_ERR_SHAPE;
+    const int st = check_args(q, k, v, out, lse, dout, dq, dk, dv, B, H, N, d, causal, scale, dtype);
+    if (st != ATTN_OK) return st;
+    const int dev_status = check_device();
+    if (dev_status != ATTN_OK) return dev_status;
+    float* delta = device_scratch();
+    if (delta == nullptr) return ATTN_ERR_DEVICE;
+    // every D_i the dK/dV kernel reads is written by the dQ kernel of the same call
+    // first, so nothing of the previous call's contents needs clearing
+    return run(q, k, v, out, lse, dout, dq, dk, dv, delta, B, H, N, d, causal, scale, dtype, stream);
 }

@@ -61,6 +61,29 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* out, const
              void* dq, void* dk, void* dv, void* delta, int B, int H, int N, int d, int causal, float scale, int dtype,
              void* stream);
 
+/* Rows (B*H*N) of D_i that attn_bwd_noalloc can hold: 4 Mi rows, 16 MiB per GPU. */
+#define ATTN_BWD_NOALLOC_MAX_ROWS 4194304
+
+/*
+ * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and gradients, without the delta workspace.  D_i
+ * goes to a device array the library owns, one per GPU, of
+ * ATTN_BWD_NOALLOC_MAX_ROWS floats (16 MiB), reserved when the library's code is
+ * loaded on that GPU and held until the process ends.  The call itself
+ * allocates nothing; its first call on a device looks up that device's array
+ * address once.
+ *
+ * Arguments, layout, ownership and status codes as for attn_bwd (without
+ * delta), plus ATTN_ERR_SHAPE when B*H*N exceeds ATTN_BWD_NOALLOC_MAX_ROWS and
+ * ATTN_ERR_DEVICE when the array's address cannot be obtained.  Every call on a
+ * GPU shares that GPU's array: calls that overlap on one GPU (on different
+ * streams, or from threads without ordering) race; order them on one stream.
+ */
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* out, const void* lse,
+                     const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d, int causal,
+                     float scale, int dtype, void* stream);
+
 /*
  * attn_lse_merge -- combine G partial results over disjoint key shards.
  *

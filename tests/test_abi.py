@@ -40,8 +40,9 @@ def declared_enum(name_prefix, header=HEADER):
 
 def test_header_declares_entry_points():
     assert declared_functions([HEADER]) == ["attn_fwd", "attn_fwd_schedule", "attn_fwd_window", "attn_status_string"]
-    assert declared_functions() == ["attn_bwd", "attn_fwd", "attn_fwd_schedule", "attn_fwd_window",
-                                    "attn_lse_merge", "attn_status_string", "gemm_bias_act", "softmax_rows"]
+    assert declared_functions() == ["attn_bwd", "attn_bwd_noalloc", "attn_fwd", "attn_fwd_schedule",
+                                    "attn_fwd_window", "attn_lse_merge", "attn_status_string", "gemm_bias_act",
+                                    "softmax_rows"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -276,3 +277,35 @@ def test_bwd_and_merge_valid_arguments_reach_the_device_check(lib):
         pytest.skip("device check refuses only where no gfx950 is current")
     assert call_bwd(lib) == 7 and call_bwd(lib, causal=0, d=80, scale=-0.3) == 7
     assert call_merge(lib) == 7 and call_merge(lib, G=1, R=1, d=64) == 7
+
+
+def call_bwd_noalloc(lib, **kw):
+    a = dict(q=A, k=A + SZ, v=A + 2 * SZ, out=A + 3 * SZ, lse=A + 4 * SZ, dout=A + 5 * SZ, dq=A + 6 * SZ,
+             dk=A + 7 * SZ, dv=A + 8 * SZ, B=1, H=2, N=16, d=64, causal=1, scale=0.125, dtype=1)
+    a.update(kw)
+    return lib.attn_bwd_noalloc(a["q"], a["k"], a["v"], a["out"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"],
+                                a["B"], a["H"], a["N"], a["d"], a["causal"], a["scale"], a["dtype"], None)
+
+
+def noalloc_max_rows():
+    text = open(os.path.join(ROOT, "include", "attn_bwd.h")).read()
+    return int(re.search(r"#define\s+ATTN_BWD_NOALLOC_MAX_ROWS\s+(\d+)", text).group(1))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(dv=None), 1), (dict(B=0), 2), (dict(d=96), 3), (dict(dtype=2), 4),
+    (dict(scale=math.nan), 5), (dict(q=A + 8), 6), (dict(causal=3), 9), (dict(dq=A + 64), 10),
+    (dict(B=1, H=1, N=4194305), 2), (dict(B=2, H=4, N=524289), 2),
+])
+def test_bwd_noalloc_argument_validation(lib, kw, code):
+    assert noalloc_max_rows() == 4194304   # the row limit the cases above straddle
+    assert call_bwd_noalloc(lib, **kw) == code, eta.attn_status_string(code)
+
+
+def test_bwd_noalloc_valid_arguments_reach_the_device_check(lib):
+    if gpu_available():
+        pytest.skip("device check refuses only where no gfx950 is current")
+    assert call_bwd_noalloc(lib) == 7
+    big = 1 << 30   # buffers of 512 MiB, kept disjoint
+    ptrs = {n: A + i * big for i, n in enumerate(("q", "k", "v", "out", "lse", "dout", "dq", "dk", "dv"))}
+    assert call_bwd_noalloc(lib, B=1, H=1, N=4194304, d=64, **ptrs) == 7   # exactly at the limit
