@@ -164,11 +164,10 @@ def traffic_summary(attn_fetch, attn_write, copy_fetch, copy_write, workload, ca
 SETTLE_S = 0.25   # minimum untimed warm-up time: the GPU clock ramps up over the first ~100 ms of load
 
 
-def warm_up(call, steps: int, sampler=None) -> dict:
+def warm_up(call, steps: int) -> dict:
     """Run `steps` untimed warm-up steps, then keep going until SETTLE_S seconds of
-    warm-up have passed, so that the timed steps see a settled clock.  The clock
-    sampler, if given, is started for the last 0.1 s.  Returns what was done
-    (reported in the JSON line)."""
+    warm-up have passed, so that the timed steps see a settled clock.  Returns what
+    was done (reported in the JSON line)."""
     import torch
     t0 = time.perf_counter()
     for _ in range(steps):
@@ -176,79 +175,11 @@ def warm_up(call, steps: int, sampler=None) -> dict:
     torch.cuda.synchronize()
     extra = 0
     while time.perf_counter() - t0 < SETTLE_S:
-        if sampler is not None and sampler._thread is None and time.perf_counter() - t0 >= SETTLE_S - 0.1:
-            sampler.start()
         for _ in range(10):
             call()
         extra += 10
         torch.cuda.synchronize()
-    if sampler is not None and sampler._thread is None:
-        sampler.start()
     return {"steps": steps, "extra_settle_steps": extra, "seconds": round(time.perf_counter() - t0, 3)}
-
-
-class SclkSampler:
-    """Samples the GPU's graphics clock (amdsmi gpu metrics, MHz, per XCD where the
-    driver reports it) from a background thread while kernels run, so the JSON line
-    states the clock the percentages of peak were measured at."""
-
-    def __init__(self, period_s: float = 0.001):
-        import threading
-        self.period_s = period_s
-        self.samples = []
-        self.error = None
-        self._stop = threading.Event()
-        self._thread = None
-        self._handle = None
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            handles = amdsmi.amdsmi_get_processor_handles()
-            if not handles:
-                raise RuntimeError("amdsmi sees no GPU")
-            self._amdsmi = amdsmi
-            self._handle = handles[0]
-            self._read()   # fail here, not in the thread
-        except Exception as e:   # the clock is context; its absence must not stop the benchmark
-            self.error = f"{type(e).__name__}: {e}"
-            self._handle = None
-
-    def _read(self):
-        m = self._amdsmi.amdsmi_get_gpu_metrics_info(self._handle)
-        clks = [c for c in (m.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
-        if clks:
-            return float(sum(clks)) / len(clks)
-        c = m.get("current_gfxclk")
-        return float(c) if isinstance(c, (int, float)) and c > 0 else None
-
-    def _run(self):
-        while not self._stop.is_set():
-            try:
-                v = self._read()
-                if v is not None:
-                    self.samples.append(v)
-            except Exception as e:
-                self.error = f"{type(e).__name__}: {e}"
-                return
-            self._stop.wait(self.period_s)
-
-    def start(self):
-        import threading
-        if self._handle is not None:
-            self._thread = threading.Thread(target=self._run, daemon=True)
-            self._thread.start()
-        return self
-
-    def stop(self) -> dict:
-        if self._thread is not None:
-            self._stop.set()
-            self._thread.join()
-        if not self.samples:
-            return {"median_mhz": None, "samples": 0, "error": self.error or "no samples"}
-        v = sorted(self.samples)
-        return {"median_mhz": round(statistics.median(v), 1), "min_mhz": round(v[0], 1), "max_mhz": round(v[-1], 1),
-                "samples": len(v), "source": "amdsmi gpu metrics current_gfxclks (mean over XCDs), sampled every 1 ms",
-                "window": "the last ~0.1 s of warm-up, the timed steps and the per-launch loop"}
 
 
 def time_steps(call, steps: int, stream) -> dict:
@@ -381,10 +312,9 @@ def bench_softmax(args, w):
     x = aw.make_rows(w.rows, w.cols, w.dtype, w.seed, w.sigma).to(dev)
     y = torch.empty_like(x)
     stream = torch.cuda.current_stream()
-    sampler = SclkSampler()
-    warm = warm_up(lambda: eta.softmax_rows(x, y, stream=stream), args.warmup, sampler)
+    warm = warm_up(lambda: eta.softmax_rows(x, y, stream=stream), args.warmup)
     t = time_steps(lambda: eta.softmax_rows(x, y, stream=stream), args.steps, stream)
-    sclk = sampler.stop()
+    sclk = ClockUnderLoad().measure(lambda: eta.softmax_rows(x, y, stream=stream))
     ms_per_step, launch_ms = t["ms_per_step"], t["launch_ms"]
     nbytes = w.algorithmic_bytes()
     value = nbytes / (ms_per_step * 1e-3) / 1e9
@@ -458,10 +388,9 @@ def bench_gemm(args, w):
     def call():
         eta.gemm_bias_act(a, b, bias, w.act, w.b_layout, c=c, stream=stream)
 
-    sampler = SclkSampler()
-    warm = warm_up(call, args.warmup, sampler)
+    warm = warm_up(call, args.warmup)
     t = time_steps(call, args.steps, stream)
-    sclk = sampler.stop()
+    sclk = ClockUnderLoad().measure(call)
     ms_per_step, launch_ms = t["ms_per_step"], t["launch_ms"]
     flops = w.flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -512,10 +441,9 @@ def bench_backward(args, w, causal):
     def call():
         eta.attn_bwd(q, k, v, out, lse, do, dq, dk, dv, delta, causal=bool(causal), scale=w.scale, stream=stream)
 
-    sampler = SclkSampler()
-    warm = warm_up(call, args.warmup, sampler)
+    warm = warm_up(call, args.warmup)
     t = time_steps(call, args.steps, stream)
-    sclk = sampler.stop()
+    sclk = ClockUnderLoad().measure(call)
     ms_per_step, launch_ms = t["ms_per_step"], t["launch_ms"]
     flops = 2.5 * w.flops(causal)
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -571,10 +499,9 @@ def bench_merge(args, w, G):
     def call():
         eta.attn_lse_merge(o_parts, l_parts, o, lse, stream=stream)
 
-    sampler = SclkSampler()
-    warm = warm_up(call, args.warmup, sampler)
+    warm = warm_up(call, args.warmup)
     t = time_steps(call, args.steps, stream)
-    sclk = sampler.stop()
+    sclk = ClockUnderLoad().measure(call)
     ms_per_step, launch_ms = t["ms_per_step"], t["launch_ms"]
     rows = w.B * w.H * w.N
     nbytes = G * rows * (w.d * 2 + 4) + rows * (w.d * 2 + 4)
@@ -718,10 +645,9 @@ def main():
     def call():
         eta.attn_fwd(q, k, v, out, lse, causal, w.scale, stream=stream, window=args.window)
 
-    sampler = SclkSampler()
-    warm = warm_up(call, args.warmup, sampler)
+    warm = warm_up(call, args.warmup)
     t = time_steps(call, args.steps, stream)
-    sclk = sampler.stop()
+    sclk = ClockUnderLoad().measure(call)
     ms_per_step, launch_ms = t["ms_per_step"], t["launch_ms"]
     flops = launch_flops(w, causal, args.window)
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -746,7 +672,9 @@ def main():
                    "scale": w.scale, "layout": "[B,H,N,d] contiguous", "pct_of_mfma_peak": round(100 * value / MFMA_PEAK_TFLOPS, 2),
                    **launch_stats(t), "sclk": sclk,
                    "pct_of_peak_at_sclk": (round(100 * achieved / (MFMA_PEAK_TFLOPS * sclk["median_mhz"] / 2400.0), 2)
-                                           if sclk.get("median_mhz") else None)},
+                                           if sclk.get("median_mhz") else None),
+                   "timing": "ms_per_step: one event pair around the K timed steps; launch_ms_*: a second loop of K "
+                             "launches, each between its own events"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(w.name, causal, args.window),
