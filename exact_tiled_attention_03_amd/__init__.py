@@ -79,6 +79,7 @@ def attn_status_string(status: int) -> str:
 
 ATTN_SCHEDULE_SMALL = 0
 ATTN_SCHEDULE_WIDE = 1
+ATTN_SCHEDULE_SPLIT = 2
 
 
 def attn_fwd_schedule(B: int, H: int, N: int, d: int, causal: bool) -> int:
@@ -372,4 +373,5 @@ def linear(x, weight, bias=None, act="none", stream=None):
 
 
 __all__ = ["attn_bwd", "attn_lse_merge", "gemm_bias_act", "linear", "GEMM_ACT", "attn_fwd", "attn_fwd_schedule", "attn_status_string", "attention", "softmax_rows", "load_library",
-           "AttnError", "ATTN_F16", "ATTN_BF16", "ATTN_F32", "ATTN_SCHEDULE_SMALL", "ATTN_SCHEDULE_WIDE"]
+           "AttnError", "ATTN_F16", "ATTN_BF16", "ATTN_F32", "ATTN_SCHEDULE_SMALL", "ATTN_SCHEDULE_WIDE",
+           "ATTN_SCHEDULE_SPLIT"]

@@ -148,9 +148,10 @@ __device__ __forceinline__ int kperm(int m) {
 //    granule per 32 lanes: the granule index g of row r sits at g ^ vswz(r),
 //    vswz(r) = (r / RPB) % GPR with GPR granules per row.  It only moves whole
 //    granules, so rows 4 apart differ by a fixed offset for every lane.
-template <int D, int WAVES_, int STAGES_ = 2> struct Cfg {
+template <int D, int WAVES_, int STAGES_ = 2, int SUBS_ = 1> struct Cfg {
     static constexpr int WAVES = WAVES_;
     static constexpr int STAGES = STAGES_;            // K/V tile stages in LDS
+    static constexpr int SUBS = SUBS_;                // tiles per stage (2: the key-split schedule)
     static constexpr int NT = 64 * WAVES;             // threads per work-group
     static constexpr int BM = 32 * WAVES;             // queries per work-group (32 per wave)
     static constexpr int BN = 64;                     // keys per tile
@@ -164,16 +165,17 @@ template <int D, int WAVES_, int STAGES_ = 2> struct Cfg {
     static constexpr int RPB = 256 / ROWB;            // rows per 256-byte bank line
     static constexpr int GPR = CPRP / 4;              // 64-byte granules per row
     static constexpr int TILEB = BN * ROWB;           // bytes of one K or V tile
-    static constexpr int KOFF = 0;                    // K stage s at KOFF + s * TILEB
-    static constexpr int VOFF = STAGES * TILEB;       // V stage s at VOFF + s * TILEB
-    static constexpr int LDS = 2 * STAGES * TILEB;
+    static constexpr int SSTR = SUBS * TILEB;         // bytes of one K (or V) stage
+    static constexpr int KOFF = 0;                    // K stage s at KOFF + s * SSTR (+ sub * TILEB)
+    static constexpr int VOFF = STAGES * SSTR;        // V stage s at VOFF + s * SSTR (+ sub * TILEB)
+    static constexpr int LDS = 2 * STAGES * SSTR;
     static constexpr int IT = TILEB / (16 * NT);      // direct-load instructions per tile and thread
     static __device__ __forceinline__ int kswz(int r) { return (r / RPB) % CPRP; }
     static __device__ __forceinline__ int vswz(int r) { return (r / RPB) % GPR; }
     static_assert(D % 16 == 0 && CPR <= CPRP, "head dim");
     static_assert(IT >= 1 && TILEB % (16 * NT) == 0, "a tile is a whole number of load rounds");
     static_assert(DBLK <= GPR, "transpose reads of the padded head dim stay inside a row");
-    static_assert(STAGES == 3 || VOFF + 2 * TILEB <= 65536, "LDS offsets fit the 16-bit immediate");
+    static_assert(STAGES == 3 || VOFF + 2 * SSTR <= 65536, "LDS offsets fit the 16-bit immediate");
     static_assert(LDS <= 160 * 1024, "LDS");
     static_assert(WAVES * 32 * ROWB <= LDS, "the epilogue's per-wave O slices fit in the stages");
 };
@@ -211,9 +213,9 @@ __device__ __forceinline__ void map_workgroup(const FwdArgs& a, int L, int& bh, 
 
 // State and arithmetic of one wave: 32 query rows (one per accumulator column;
 // the two lanes of a column each hold half of the keys of a tile).
-template <int D, int DT, bool CAUSAL, int WAVES, bool WIN, int STAGES = 2>
+template <int D, int DT, bool CAUSAL, int WAVES, bool WIN, int STAGES = 2, int SUBS = 1>
 struct Wave {
-    using C = Cfg<D, WAVES, STAGES>;
+    using C = Cfg<D, WAVES, STAGES, SUBS>;
     using E = Elem<DT>;
     static constexpr int SB = C::SB, KK = C::KK, KSTEPS = C::KSTEPS, DBLK = C::DBLK, CPR = C::CPR;
 
@@ -229,7 +231,9 @@ struct Wave {
     f32x16_t o[DBLK];                  // O^T accumulator
     float m, l;                        // reference max (log2 units) and this half's sum
 
-    __device__ __forceinline__ void init(const FwdArgs& a, unsigned lds_base, int tid, int wave_) {
+    // sub: the tile of each stage this wave reads (the key-split schedule's second
+    // pair of waves reads the second tile)
+    __device__ __forceinline__ void init(const FwdArgs& a, unsigned lds_base, int tid, int wave_, int sub = 0) {
         lane = tid & 63;
         wave = wave_;
         hf = lane >> 5;
@@ -255,7 +259,8 @@ struct Wave {
             const int r = kperm(n);
             const int x = C::kswz(r);                              // rows r and r + 32 share it
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) ka[ks] = lds0 + C::KOFF + r * C::ROWB + (((2 * ks + hf) ^ x) * 16);
+            for (int ks = 0; ks < KSTEPS; ++ks)
+                ka[ks] = lds0 + C::KOFF + sub * C::TILEB + r * C::ROWB + (((2 * ks + hf) ^ x) * 16);
         }
         {
             const int g16 = lane >> 4, s16 = lane & 15;
@@ -263,7 +268,8 @@ struct Wave {
             const int x = C::vswz(r);                             // the same for r + 16*kk + 4*half
 #pragma unroll
             for (int db = 0; db < DBLK; ++db)
-                va[db] = lds0 + C::VOFF + r * C::ROWB + (4 * (db ^ x) + 2 * (g16 & 1) + ((s16 & 3) >> 1)) * 16 + 8 * (s16 & 1);
+                va[db] = lds0 + C::VOFF + sub * C::TILEB + r * C::ROWB + (4 * (db ^ x) + 2 * (g16 & 1) + ((s16 & 3) >> 1)) * 16 +
+                         8 * (s16 & 1);
         }
     }
 
@@ -282,12 +288,13 @@ struct Wave {
     }
 
     // this wave's share of tile j of K (is_v false) or V into LDS stage `stage`
-    __device__ __forceinline__ void issue(bool is_v, int j, int stage) const {
+    // (its tile `sub` in the key-split schedule)
+    __device__ __forceinline__ void issue(bool is_v, int j, int stage, int sub = 0) const {
         const int kt0 = j * C::BN;
         const int bytes = (N - kt0) * D * 2;            // rows kt0 .. N-1 are in range
         const unsigned char* base = (is_v ? vbase : kbase) + (size_t)kt0 * D * 2;
         const eta_desc_t desc = buffer_desc(base, bytes);
-        const unsigned region = lds0 + (is_v ? C::VOFF : C::KOFF) + stage * C::TILEB;
+        const unsigned region = lds0 + (is_v ? C::VOFF : C::KOFF) + stage * C::SSTR + sub * C::TILEB;
 #pragma unroll
         for (int it = 0; it < C::IT; ++it)
             load_lds16(desc, is_v ? vvo[it] : kvo[it], 0, region + (unsigned)(slot_base(it) * 16));
@@ -342,7 +349,7 @@ struct Wave {
         for (int ks = 0; ks < KSTEPS; ++ks)
 #pragma unroll
             for (int sb = 0; sb < SB; ++sb)
-                s[sb] = E::mfma(lds_read16(ka[ks] + ST * C::TILEB + sb * 32 * C::ROWB), qf[ks], s[sb]);
+                s[sb] = E::mfma(lds_read16(ka[ks] + ST * C::SSTR + sb * 32 * C::ROWB), qf[ks], s[sb]);
     }
 
     // Mask tile j's scores where needed and update the reference max.  m is
@@ -411,8 +418,8 @@ struct Wave {
         for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
             for (int db = 0; db < DBLK; ++db) {
-                const u32x2_t lo = lds_read_tr(va[db] + ST * C::TILEB + 16 * kk * C::ROWB);
-                const u32x2_t hi = lds_read_tr(va[db] + ST * C::TILEB + (16 * kk + 4) * C::ROWB);
+                const u32x2_t lo = lds_read_tr(va[db] + ST * C::SSTR + 16 * kk * C::ROWB);
+                const u32x2_t hi = lds_read_tr(va[db] + ST * C::SSTR + (16 * kk + 4) * C::ROWB);
                 o[db] = E::mfma(u32x4_t{lo[0], lo[1], hi[0], hi[1]}, pf[kk], o[db]);
             }
     }
@@ -430,11 +437,11 @@ struct Wave {
         auto rd = [&](int r) {
             if (r < NPV) {
                 const int kk = r / DBLK, db = r % DBLK;
-                const u32x2_t lo = lds_read_tr(va[db] + ST * C::TILEB + 16 * kk * C::ROWB);
-                const u32x2_t hi = lds_read_tr(va[db] + ST * C::TILEB + (16 * kk + 4) * C::ROWB);
+                const u32x2_t lo = lds_read_tr(va[db] + ST * C::SSTR + 16 * kk * C::ROWB);
+                const u32x2_t hi = lds_read_tr(va[db] + ST * C::SSTR + (16 * kk + 4) * C::ROWB);
                 vo[r & 1] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
             }
-            if (r < NSC) ko[r & 1] = lds_read16(ka[r / SB] + ST1 * C::TILEB + (r % SB) * 32 * C::ROWB);
+            if (r < NSC) ko[r & 1] = lds_read16(ka[r / SB] + ST1 * C::SSTR + (r % SB) * 32 * C::ROWB);
         };
 #pragma unroll
         for (int sb = 0; sb < SB; ++sb) s[sb] = f32x16_t{};
@@ -510,12 +517,22 @@ struct Wave {
 template <int WAVES> constexpr bool fwd_ping() { return WAVES == 8; }
 template <int WAVES> constexpr int fwd_stages() { return fwd_ping<WAVES>() ? 3 : 2; }
 
-template <int D, int DT, bool CAUSAL, int WAVES, bool WIN>
+// SPLIT (8 waves, no window): the key-split form of the two-group schedule.
+// A work-group owns 128 query rows; wave w and wave w+4 hold the same 32 rows,
+// group 0 over the first half of the item's key tiles and group 1 over the
+// second half, each LDS stage holding one tile of each half; the two partial
+// results of a row are merged through LDS at the end of the item.  Used for
+// short problems where one 256-query work-group per CU would leave CUs idle
+// and the 4-wave grid would leave them with one wave per SIMD.
+template <int D, int DT, bool CAUSAL, int WAVES, bool WIN, bool SPLIT = false>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
+    static_assert(!SPLIT || (WAVES == 8 && !WIN), "the key split is a form of the 8-wave schedule without a window");
     constexpr int STAGES = fwd_stages<WAVES>();
-    using C = Cfg<D, WAVES, STAGES>;
+    constexpr int SUBS = SPLIT ? 2 : 1;
+    using C = Cfg<D, WAVES, STAGES, SUBS>;
+    constexpr int BMQ = SPLIT ? 128 : C::BM;                // query rows per work item
     // the two-group schedule adds room for the Q slices of waves 4-7 (waves 0-3
     // use the K and V areas of stage 2, free while a query tile's loads start)
     constexpr int QEXTRA = fwd_ping<WAVES>() ? 4 * 32 * C::ROWB : 0;
@@ -523,8 +540,9 @@ void attn_fwd_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[C::LDS + QEXTRA];
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    Wave<D, DT, CAUSAL, WAVES, WIN, STAGES> w;
-    w.init(a, (unsigned)(size_t)(lds_bytes)smem, tid, wave);
+    Wave<D, DT, CAUSAL, WAVES, WIN, STAGES, SUBS> w;
+    const int half = SPLIT ? wave >> 2 : 0;                       // key half of this wave (key split)
+    w.init(a, (unsigned)(size_t)(lds_bytes)smem, tid, wave, half);
 
     // Work units (a query tile, or a causal pair of them) blockIdx.x,
     // blockIdx.x + gridDim.x, ...: the grid is either one work-group per unit
@@ -537,13 +555,13 @@ void attn_fwd_kernel(FwdArgs a) {
     const int nitems = CAUSAL && grp != a.nqt - 1 - grp ? 2 : 1;
     for (int item = 0; item < nitems; ++item, first = false) {
         const int qt = CAUSAL ? (item == 0 ? a.nqt - 1 - grp : grp) : grp;
-        const int q0 = qt * C::BM;
-        // Q rows come through LDS (q_issue / q_read) in both schedules
-        w.begin(a, bh, q0 + 32 * wave);
+        const int q0 = qt * BMQ;
+        // Q rows come through LDS (q_issue / q_read) in every schedule
+        w.begin(a, bh, q0 + 32 * (SPLIT ? wave & 3 : wave));
         // key tiles jlo .. nt-1: up to the last query (causal) or its band's end,
         // from the first query's band start
         const int win = WIN ? a.window : 0;
-        const int kend = CAUSAL ? min(a.N, q0 + C::BM) : (win > 0 ? min(a.N, q0 + C::BM - 1 + win) : a.N);
+        const int kend = CAUSAL ? min(a.N, q0 + BMQ) : (win > 0 ? min(a.N, q0 + BMQ - 1 + win) : a.N);
         const int nt = (kend + C::BN - 1) / C::BN;
         const int jlo = win > 0 ? max(0, q0 - win + 1) / C::BN : 0;
 
@@ -563,9 +581,18 @@ void attn_fwd_kernel(FwdArgs a) {
             // start of slot 2u+1 into the stage of tile u-1, whose V was last
             // read in slot 2u, and every wave waits for its share at the end of
             // slot 2u+2, before that tile's K is first read in slot 2u+3.
+            // With the key split, step u of group g works on key tile jlo + g H + u
+            // (H = the first half's tile count) and stage u % 3 holds both groups'
+            // tiles of step u.
             if (!first) __syncthreads();                   // every wave has left the previous item's tiles
             const bool g0 = wave < 4;                      // wave-uniform
-            const int T = nt - jlo;
+            const int TI = nt - jlo;                       // key tiles of the item
+            const int H = SPLIT ? (TI + 1) / 2 : TI;       // steps (the first half's tiles)
+            const int T = H;
+            const int j0 = jlo + half * H;                 // this wave's first tile
+            const int jend = SPLIT && half == 0 ? jlo + H : nt;
+            // keys for this wave in step u (without the split every step has a tile: testing it spills registers)
+            auto has = [&](int u) { return (!SPLIT || j0 + u < jend) && w.active(j0 + u); };
             f32x16_t s[C::SB];                             // scores of the tile whose softmax is next
             u32x4_t pf[C::KK];                             // P of the tile whose P.V is next
             // One code path for the matrix half keeps register use low: a wave
@@ -573,7 +600,7 @@ void attn_fwd_kernel(FwdArgs a) {
             // past the wave's last tile is not used.
             auto X = [&](auto stage_tag, int u) {
                 constexpr int ST = decltype(stage_tag)::value, ST1 = (ST + 1) % 3;
-                const bool do_pv = w.active(jlo + u), do_s = u + 1 < T && w.active(jlo + u + 1);
+                const bool do_pv = has(u), do_s = u + 1 < T && has(u + 1);
                 if (do_pv || do_s) {
                     if (!do_pv) {
 #pragma unroll
@@ -584,17 +611,20 @@ void attn_fwd_kernel(FwdArgs a) {
                     __builtin_amdgcn_s_setprio(0);
                 }
             };
+            // the tiles of step t into stage `stage`: K (is_v false) or V
+            auto issue_step = [&](bool is_v, int t, int stage) {
+                if (t < H) w.issue(is_v, jlo + t, stage, 0);
+                if (SPLIT && H + t < TI) w.issue(is_v, jlo + H + t, stage, 1);
+            };
             auto issue_tile = [&](auto stage_tag, int u) {
                 constexpr int ST2 = (decltype(stage_tag)::value + 2) % 3;
-                if (u + 2 < T) {
-                    w.issue(false, jlo + u + 2, ST2);
-                    w.issue(true, jlo + u + 2, ST2);
-                }
+                issue_step(false, u + 2, ST2);
+                issue_step(true, u + 2, ST2);
             };
             auto tile = [&](auto stage_tag, int u) {
                 if (!g0) issue_tile(stage_tag, u);          // slot 2u+1 starts (group 1)
-                if (w.active(jlo + u)) {
-                    w.prepare(s, jlo + u);
+                if (has(u)) {
+                    w.prepare(s, j0 + u);
                     w.probs(s, pf);
                 }
                 if (g0) wait_loads();                       // slot 2u ends (group 0): tile u+1 landed
@@ -608,24 +638,39 @@ void attn_fwd_kernel(FwdArgs a) {
             // the extra room past the stages (4-7); stage 2 first receives a tile
             // after the barrier below
             const unsigned lds_base = (unsigned)(size_t)(lds_bytes)smem;
-            const unsigned qslice = lds_base + (unsigned)((wave < 2   ? C::KOFF + 2 * C::TILEB + wave * 32 * C::ROWB
-                                                           : wave < 4 ? C::VOFF + 2 * C::TILEB + (wave - 2) * 32 * C::ROWB
+            const unsigned qslice = lds_base + (unsigned)((wave < 2   ? C::KOFF + 2 * C::SSTR + wave * 32 * C::ROWB
+                                                           : wave < 4 ? C::VOFF + 2 * C::SSTR + (wave - 2) * 32 * C::ROWB
                                                                       : C::LDS + (wave - 4) * 32 * C::ROWB));
             if (w.qw0 < a.N) w.q_issue(a, bh, qslice);
-            w.issue(false, jlo, 0);
-            w.issue(true, jlo, 0);
-            if (T > 1) {
-                w.issue(false, jlo + 1, 1);
-                w.issue(true, jlo + 1, 1);
+            issue_step(false, 0, 0);
+            issue_step(true, 0, 0);
+            issue_step(false, 1, 1);
+            issue_step(true, 1, 1);
+            // only Q and step 0's K are needed for the first scores: step 0's V and
+            // step 1's tiles (issued after them) are waited for before the barrier
+            // that ends slot 0 (group 0 in its first tile step, group 1 just below)
+            {
+                const int tiles0 = SPLIT && H < TI ? 2 : 1;                  // tiles in step 0
+                const int tiles1 = (1 < H ? 1 : 0) + (SPLIT && H + 1 < TI ? 1 : 0);
+                const int after = (SPLIT ? tiles0 : 1) + 2 * tiles1;          // K/V loads issued after step 0's K
+                if (!SPLIT) {
+                    if (T > 1) wait_vmcnt<3 * C::IT>();
+                    else wait_vmcnt<C::IT>();
+                } else if (tiles0 == 2) {
+                    // order: K0a, K0b, V0a, V0b, K1a, K1b, V1a, V1b; wait for Q, K0a, K0b
+                    // (each wave's loads complete in order: K0b is the second K)
+                    if (after >= 6) wait_vmcnt<6 * C::IT>();
+                    else if (after >= 4) wait_vmcnt<4 * C::IT>();
+                    else if (after >= 3) wait_vmcnt<3 * C::IT>();
+                    else wait_vmcnt<2 * C::IT>();
+                } else {
+                    if (after >= 3) wait_vmcnt<3 * C::IT>();
+                    else wait_vmcnt<C::IT>();
+                }
             }
-            // only Q and tile 0's K are needed for the first scores: tile 0's V and
-            // tile 1 (issued after them) are waited for before the barrier that
-            // ends slot 0 (group 0 in its first tile step, group 1 just below)
-            if (T > 1) wait_vmcnt<3 * C::IT>();
-            else wait_vmcnt<C::IT>();
             w.q_read(a, qslice);                           // this wave's own loads: no barrier needed
             __syncthreads();
-            if (w.active(jlo)) w.template score<0>(s);
+            if (has(0)) w.template score<0>(s);
             if (!g0) {
                 wait_loads();
                 __syncthreads();
@@ -636,7 +681,40 @@ void attn_fwd_kernel(FwdArgs a) {
                 if (u + 2 < T) tile(std::integral_constant<int, 2>{}, u + 2);
             }
             if (g0) __syncthreads();
-            w.finish(a, bh);
+            if constexpr (SPLIT) {
+                // group 1 hands its partial (m, l, O^T) to the group-0 wave with the same
+                // rows through the V stages (idle now; the epilogue's slices lie in the K
+                // stages): register i of lane L at float i * 64 + L of the wave's area
+                constexpr int NV = 16 * C::DBLK + 2;       // floats per lane
+                static_assert(4 * NV * 64 * 4 <= C::STAGES * C::SSTR, "merge areas fit the V stages");
+                float* area = reinterpret_cast<float*>(smem + C::VOFF) + (wave & 3) * NV * 64;
+                const int ln = tid & 63;
+                if (!g0) {
+#pragma unroll
+                    for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) area[(16 * db + i) * 64 + ln] = w.o[db][i];
+                    area[(NV - 2) * 64 + ln] = w.m;
+                    area[(NV - 1) * 64 + ln] = w.l;
+                }
+                __syncthreads();
+                if (g0) {
+                    // m in log2 units; a half with no kept key has m = -inf, l = 0, O = 0
+                    const float mb = area[(NV - 2) * 64 + ln], lb = area[(NV - 1) * 64 + ln];
+                    const float mm = fmaxf(w.m, mb);
+                    const float fa = mm > kNegInf ? __builtin_amdgcn_exp2f(w.m - mm) : 0.f;
+                    const float fb = mm > kNegInf ? __builtin_amdgcn_exp2f(mb - mm) : 0.f;
+#pragma unroll
+                    for (int db = 0; db < C::DBLK; ++db)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) w.o[db][i] = w.o[db][i] * fa + area[(16 * db + i) * 64 + ln] * fb;
+                    w.l = w.l * fa + lb * fb;
+                    w.m = mm;
+                    w.finish(a, bh);
+                }
+            } else {
+                w.finish(a, bh);
+            }
             continue;
         }
 
@@ -667,8 +745,8 @@ void attn_fwd_kernel(FwdArgs a) {
         // the Q slices of the 4-wave kernel: stage 1's K area (waves 0, 1) and V
         // area (2, 3); stage 1 first receives a tile after the barrier below
         const unsigned qslice = (unsigned)(size_t)(lds_bytes)smem +
-                                (unsigned)(wave < 2 ? C::KOFF + C::TILEB + wave * 32 * C::ROWB
-                                                    : C::VOFF + C::TILEB + (wave - 2) * 32 * C::ROWB);
+                                (unsigned)(wave < 2 ? C::KOFF + C::SSTR + wave * 32 * C::ROWB
+                                                    : C::VOFF + C::SSTR + (wave - 2) * 32 * C::ROWB);
         if (w.qw0 < a.N) w.q_issue(a, bh, qslice);           // four Q slices fill stage 1
         w.issue(false, jlo, 0);
         w.issue(true, jlo, 0);
@@ -697,24 +775,43 @@ bool use_wide(long long bh, long long N, int causal) {
     return (causal ? (nqt + 1) / 2 : nqt) * bh >= kWideMinGroups;
 }
 
+// The key-split form of the 8-wave schedule (d = 64: its stages of two tiles
+// fit the LDS; no window) where the 4-wave grid would leave CUs with one
+// work-group, i.e. one wave per SIMD (fewer than two work-groups per CU of a
+// 256-CU MI355X), and the query tiles are long: measured against the 4-wave
+// schedule, +6.6% at B=1 H=16 N=4096 causal and +3.2% at B=2 H=16 N=2048
+// causal, but -4% at N=1024 and -18% at N=128, where the fixed cost of each
+// query tile (first loads, merge, epilogue) outweighs the overlap it gains.
+constexpr long long kSplitBelowGroups = 512;
+constexpr long long kSplitMinN = 2048;
+
+bool use_split(long long bh, long long N, int d, int causal, int window) {
+    if (d != 64 || window > 0 || N < kSplitMinN || use_wide(bh, N, causal)) return false;
+    const long long nqt = (N + 127) / 128;
+    return (causal ? (nqt + 1) / 2 : nqt) * bh < kSplitBelowGroups;
+}
+
 // Resident work-groups for the 8-wave schedule: one per CU (its LDS stages
 // leave room for no second one), each looping over work units, so that the
 // grid runs as one round instead of several.
 
-template <int D, int DT, bool CAUSAL, int WAVES, bool WIN>
+template <int D, int DT, bool CAUSAL, int WAVES, bool WIN, bool SPLIT = false>
 hipError_t launch_waves(FwdArgs a, hipStream_t stream, int cus) {
-    constexpr int BM = Cfg<D, WAVES>::BM;
+    constexpr int BM = SPLIT ? 128 : Cfg<D, WAVES>::BM;
     const long long nqt = ((long long)a.N + BM - 1) / BM;
     a.nqt = (int)nqt;
     a.ngroups = CAUSAL ? (int)((nqt + 1) / 2) : (int)nqt;
     const unsigned units = (unsigned)a.ngroups * (unsigned)a.BH;
     unsigned grid = units;
     if (fwd_ping<WAVES>() && cus >= 8 && units > (unsigned)cus) grid = (unsigned)cus & ~7u;
-    return launch_kernel(attn_fwd_kernel<D, DT, CAUSAL, WAVES, WIN>, dim3(grid), dim3(64 * WAVES), stream, a);
+    return launch_kernel(attn_fwd_kernel<D, DT, CAUSAL, WAVES, WIN, SPLIT>, dim3(grid), dim3(64 * WAVES), stream, a);
 }
 
 template <int D, int DT, bool CAUSAL>
 hipError_t launch(FwdArgs a, hipStream_t stream, int cus) {
+    if constexpr (D == 64) {
+        if (use_split(a.BH, a.N, D, CAUSAL, a.window)) return launch_waves<D, DT, CAUSAL, 8, false, true>(a, stream, cus);
+    }
     const bool wide = use_wide(a.BH, a.N, CAUSAL);
     if (a.window > 0)
         return wide ? launch_waves<D, DT, CAUSAL, 8, true>(a, stream, cus)
@@ -852,5 +949,7 @@ extern "C" int attn_fwd_window(const void* q, const void* k, const void* v, void
 extern "C" int attn_fwd_schedule(int B, int H, int N, int d, int causal) {
     const int st = check_shape(B, H, N, d, causal);
     if (st != ATTN_OK) return -st;
-    return use_wide((long long)B * H, N, causal) ? ATTN_SCHEDULE_WIDE : ATTN_SCHEDULE_SMALL;
+    const long long bh = (long long)B * H;
+    if (use_split(bh, N, d, causal, 0)) return ATTN_SCHEDULE_SPLIT;
+    return use_wide(bh, N, causal) ? ATTN_SCHEDULE_WIDE : ATTN_SCHEDULE_SMALL;
 }

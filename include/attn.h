@@ -115,18 +115,23 @@ int attn_fwd_window(const void* q, const void* k, const void* v, void* out, floa
                     void* stream);
 
 /*
- * attn_fwd_schedule -- which kernel schedule attn_fwd (and attn_fwd_window,
- * which makes the same choice) uses for a shape.
+ * attn_fwd_schedule -- which kernel schedule attn_fwd uses for a shape
+ * (attn_fwd_window makes the same choice, except that it never uses
+ * ATTN_SCHEDULE_SPLIT).
  *
  * Returns ATTN_SCHEDULE_SMALL (4 waves, 128 queries per work-group, two
- * work-groups per CU) or ATTN_SCHEDULE_WIDE (8 waves, 256 queries per
- * work-group, one per CU), or a negative attn_status for arguments
- * attn_fwd would reject by shape (ATTN_ERR_SHAPE, ATTN_ERR_HEAD_DIM,
- * ATTN_ERR_CAUSAL).  Pure host function: no device is touched.  The choice
- * depends on B*H, N and causal only; results do not depend on it beyond
- * floating-point rounding order.
+ * work-groups per CU), ATTN_SCHEDULE_WIDE (8 waves, 256 queries per
+ * work-group, one per CU), ATTN_SCHEDULE_SPLIT (d = 64 and N >= 2048 where
+ * the small schedule would give fewer than 512 work-groups: 8 waves, 128 queries per
+ * work-group, one per CU; the two waves that hold the same 32 rows each take
+ * one half of the query tile's key tiles and their partial results are merged
+ * at the end), or a negative
+ * attn_status for arguments attn_fwd would reject by shape (ATTN_ERR_SHAPE,
+ * ATTN_ERR_HEAD_DIM, ATTN_ERR_CAUSAL).  Pure host function: no device is
+ * touched.  The choice depends on B*H, N, d and causal only; results do not
+ * depend on it beyond floating-point rounding order.
  */
-typedef enum { ATTN_SCHEDULE_SMALL = 0, ATTN_SCHEDULE_WIDE = 1 } attn_schedule;
+typedef enum { ATTN_SCHEDULE_SMALL = 0, ATTN_SCHEDULE_WIDE = 1, ATTN_SCHEDULE_SPLIT = 2 } attn_schedule;
 int attn_fwd_schedule(int B, int H, int N, int d, int causal);
 
 /* Static, NUL-terminated English description of a status code (never NULL). */

@@ -132,6 +132,15 @@ def test_schedule_choice(lib):
             assert eta.attn_fwd_schedule(w.B, w.H, w.N, w.d, c) == want[w.name], (w.name, c)
     assert eta.attn_fwd_schedule(8, 64, 200, 80, 1) == 1      # 512 heads of one 256-query tile
     assert eta.attn_fwd_schedule(8, 63, 200, 80, 1) == 0
+    assert eta.ATTN_SCHEDULE_SPLIT == 2
+    # d = 64, N >= 2048, fewer than 512 work-groups of 128 queries: the key split
+    assert eta.attn_fwd_schedule(1, 16, 4096, 64, 1) == 2     # 16 pairs x 16 heads = 256
+    assert eta.attn_fwd_schedule(1, 32, 4096, 64, 1) == 0     # 512
+    assert eta.attn_fwd_schedule(1, 31, 4096, 64, 1) == 2
+    assert eta.attn_fwd_schedule(1, 15, 2048, 64, 0) == 2     # 16 tiles x 15 heads = 240
+    assert eta.attn_fwd_schedule(1, 15, 2047, 64, 0) == 0     # N below 2048
+    assert eta.attn_fwd_schedule(1, 4, 4096, 80, 1) == 0      # d = 80 never splits
+    assert eta.attn_fwd_schedule(8, 64, 2048, 64, 1) == 1     # wide wins first
     assert eta.attn_fwd_schedule(1, 1, 8, 96, 0) == -3
     assert eta.attn_fwd_schedule(0, 1, 8, 64, 0) == -2
     assert lib.attn_fwd_schedule(1, 1, 8, 64, 3) == -9   # the binding itself coerces causal to 0/1

@@ -216,3 +216,46 @@ def test_wide_schedule_long_causal_rows_and_outliers(lib):
     out, lse = run_gpu(q, k, v, 1, 1 / math.sqrt(128))
     assert_within_derived_bound(out, lse, q, k, v, 1, 1 / math.sqrt(128))
     assert torch.equal(out[:, :, 0].view(torch.int16), v[:, :, 0].view(torch.int16))
+
+
+# d = 64 shapes with N >= 2048 and fewer than 512 work-groups of 128 queries take
+# the key-split form of the 8-wave schedule: waves w and w+4 hold the same rows,
+# each over one half of the query tile's key tiles, merged at the end.  The
+# shapes give items with one tile (second half empty), odd counts (halves differ
+# by one) and even counts, ragged N and rows past N.
+SPLIT_SHAPES = [(1, 1, 2048), (1, 2, 2049), (2, 1, 2111), (1, 1, 3000)]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_key_split_schedule(lib, dtype, causal):
+    for B, H, N in SPLIT_SHAPES:
+        assert lib.attn_fwd_schedule(B, H, N, 64, causal) == lib.ATTN_SCHEDULE_SPLIT
+        print(f"\n[case] split B={B} H={H} N={N} {dtype} causal={causal}", flush=True)
+        q, k, v = aw.make_inputs((B, H, N, 64), dtype, 9500 + N)
+        out, lse = run_gpu(q, k, v, causal, 0.125)
+        assert_within_derived_bound(out, lse, q, k, v, causal, 0.125, label=f"split N={N} {dtype} causal={causal}")
+        if causal:
+            assert torch.equal(out[:, :, 0].view(torch.int16), v[:, :, 0].view(torch.int16))
+
+
+def test_key_split_merge_with_outliers(lib):
+    # the two halves reach very different row maxima: the merge rescales both
+    q, k, v = aw.make_inputs((2, 3, 2100, 64), "fp16", 9600, outlier_fraction=0.02, outlier_factor=30.0)
+    for causal in (0, 1):
+        assert lib.attn_fwd_schedule(2, 3, 2100, 64, causal) == lib.ATTN_SCHEDULE_SPLIT
+        for scale in (0.125, -0.2):
+            out, lse = run_gpu(q, k, v, causal, scale)
+            rows = np.unique(np.concatenate([np.arange(200), np.random.default_rng(5).choice(2100, 300, replace=False), [2099]]))
+            assert_within_derived_bound(out, lse, q, k, v, causal, scale, rows=rows,
+                                        label=f"split outliers causal={causal} scale={scale}")
+
+
+def test_small_schedule_d64(lib):
+    # 512 work-groups of 128 queries: the 4-wave schedule without the key split
+    for causal, (B, H, N) in ((1, (8, 32, 512)), (0, (4, 32, 512))):
+        assert lib.attn_fwd_schedule(B, H, N, 64, causal) == lib.ATTN_SCHEDULE_SMALL
+        q, k, v = aw.make_inputs((B, H, N, 64), "bf16", 9700 + causal)
+        out, lse = run_gpu(q, k, v, causal, 0.125)
+        rows = np.unique(np.concatenate([np.arange(70), np.arange(N - 70, N)]))
+        assert_within_derived_bound(out, lse, q, k, v, causal, 0.125, rows=rows, label=f"small d64 causal={causal}")
