@@ -314,7 +314,7 @@ def bench_softmax(args, w):
     stream = torch.cuda.current_stream()
     warm = warm_up(lambda: eta.softmax_rows(x, y, stream=stream), args.warmup)
     t = time_steps(lambda: eta.softmax_rows(x, y, stream=stream), args.steps, stream)
-    sclk = ClockUnderLoad().measure(lambda: eta.softmax_rows(x, y, stream=stream))
+    sclk = None if args.no_clock else ClockUnderLoad().measure(lambda: eta.softmax_rows(x, y, stream=stream))
     ms_per_step, launch_ms = t["ms_per_step"], t["launch_ms"]
     nbytes = w.algorithmic_bytes()
     value = nbytes / (ms_per_step * 1e-3) / 1e9
@@ -390,7 +390,7 @@ def bench_gemm(args, w):
 
     warm = warm_up(call, args.warmup)
     t = time_steps(call, args.steps, stream)
-    sclk = ClockUnderLoad().measure(call)
+    sclk = None if args.no_clock else ClockUnderLoad().measure(call)
     ms_per_step, launch_ms = t["ms_per_step"], t["launch_ms"]
     flops = w.flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -443,7 +443,7 @@ def bench_backward(args, w, causal):
 
     warm = warm_up(call, args.warmup)
     t = time_steps(call, args.steps, stream)
-    sclk = ClockUnderLoad().measure(call)
+    sclk = None if args.no_clock else ClockUnderLoad().measure(call)
     ms_per_step, launch_ms = t["ms_per_step"], t["launch_ms"]
     flops = 2.5 * w.flops(causal)
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -501,7 +501,7 @@ def bench_merge(args, w, G):
 
     warm = warm_up(call, args.warmup)
     t = time_steps(call, args.steps, stream)
-    sclk = ClockUnderLoad().measure(call)
+    sclk = None if args.no_clock else ClockUnderLoad().measure(call)
     ms_per_step, launch_ms = t["ms_per_step"], t["launch_ms"]
     rows = w.B * w.H * w.N
     nbytes = G * rows * (w.d * 2 + 4) + rows * (w.d * 2 + 4)
@@ -583,6 +583,8 @@ def main():
     ap.add_argument("--backward", action="store_true", help="time attn_bwd on the attention workload")
     ap.add_argument("--merge", type=int, default=0, help="time attn_lse_merge over this many key shards")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the clock-under-load window (for profiler runs, which time every dispatch)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--traffic-summary", nargs=4, metavar="DIR")
@@ -647,7 +649,7 @@ def main():
 
     warm = warm_up(call, args.warmup)
     t = time_steps(call, args.steps, stream)
-    sclk = ClockUnderLoad().measure(call)
+    sclk = None if args.no_clock else ClockUnderLoad().measure(call)
     ms_per_step, launch_ms = t["ms_per_step"], t["launch_ms"]
     flops = launch_flops(w, causal, args.window)
     value = flops / (ms_per_step * 1e-3) / 1e12
@@ -672,7 +674,7 @@ def main():
                    "scale": w.scale, "layout": "[B,H,N,d] contiguous", "pct_of_mfma_peak": round(100 * value / MFMA_PEAK_TFLOPS, 2),
                    **launch_stats(t), "sclk": sclk,
                    "pct_of_peak_at_sclk": (round(100 * achieved / (MFMA_PEAK_TFLOPS * sclk["median_mhz"] / 2400.0), 2)
-                                           if sclk.get("median_mhz") else None),
+                                           if sclk and sclk.get("median_mhz") else None),
                    "timing": "ms_per_step: one event pair around the K timed steps; launch_ms_*: a second loop of K "
                              "launches, each between its own events"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
