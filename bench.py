@@ -182,6 +182,63 @@ def warm_up(call, steps: int) -> dict:
     return {"steps": steps, "extra_settle_steps": extra, "seconds": round(time.perf_counter() - t0, 3)}
 
 
+class ClockUnderLoad:
+    """The GPU clock and power while the timed kernel runs back to back.
+
+    The driver's metrics table (amdsmi gpu metrics) is refreshed about once a
+    second, so a few milliseconds of timed steps never show in it.  measure()
+    keeps launching the same call after the timed steps until the table has
+    been refreshed twice (the second refresh then covers a whole period of
+    sustained load, at most ~3 s) and reports that snapshot: the graphics clock
+    of every XCD (MHz) and the socket power (W)."""
+
+    def __init__(self):
+        self.error = None
+        self._h = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if not handles:
+                raise RuntimeError("amdsmi sees no GPU")
+            self._amdsmi, self._h = amdsmi, handles[0]
+            self._read()
+        except Exception as e:   # the clock is context; its absence must not stop the benchmark
+            self.error = f"{type(e).__name__}: {e}"
+            self._h = None
+
+    def _read(self):
+        return self._amdsmi.amdsmi_get_gpu_metrics_info(self._h)
+
+    def measure(self, call, max_s: float = 3.0) -> dict:
+        if self._h is None:
+            return {"median_mhz": None, "error": self.error}
+        import torch
+        try:
+            stamp = self._read().get("system_clock_counter")
+            refreshes, snap, t0 = 0, None, time.perf_counter()
+            while refreshes < 2 and time.perf_counter() - t0 < max_s:
+                for _ in range(4):
+                    call()
+                torch.cuda.synchronize()
+                m = self._read()
+                if m.get("system_clock_counter") != stamp:
+                    stamp, refreshes, snap = m.get("system_clock_counter"), refreshes + 1, m
+            if refreshes < 2:
+                return {"median_mhz": None, "error": "metrics table not refreshed twice under load"}
+            clks = [float(c) for c in (snap.get("current_gfxclks") or []) if isinstance(c, (int, float)) and c > 0]
+            if not clks and isinstance(snap.get("current_gfxclk"), (int, float)):
+                clks = [float(snap["current_gfxclk"])]
+            power = snap.get("current_socket_power")
+            return {"median_mhz": round(statistics.median(clks), 1) if clks else None,
+                    "per_xcd_mhz": clks, "socket_power_w": power if isinstance(power, (int, float)) else None,
+                    "source": "amdsmi gpu metrics (current_gfxclks, current_socket_power), the second table "
+                              "refresh while the same launches ran back to back after the timed steps",
+                    "seconds_under_load": round(time.perf_counter() - t0, 2)}
+        except Exception as e:
+            return {"median_mhz": None, "error": f"{type(e).__name__}: {e}"}
+
+
 def time_steps(call, steps: int, stream) -> dict:
     """The K timed steps: one event before the first launch and one after the last,
     with a synchronize on both sides (ms_per_step = elapsed / K, nothing between the

@@ -27,3 +27,33 @@ def test_launch_flops_conventions():
     # a window of N keeps every causal pair: N(N+1)/2 per head, not the N^2/2 convention
     assert bench.launch_flops(w, 1, w.N) == 4.0 * w.d * w.B * w.H * w.N * (w.N + 1) / 2
     assert bench.launch_flops(w, 0, 1) == 4.0 * w.d * w.B * w.H * w.N
+
+
+def test_every_name_bench_reads_is_defined():
+    """Each name that bench.py loads is bound somewhere in it or is a builtin, so no
+    run of the benchmark stops on a NameError."""
+    import ast
+    import builtins
+    tree = ast.parse(open(bench.__file__).read())
+    bound = set(dir(builtins)) | {"__file__", "__name__", "__doc__"}
+    for node in ast.walk(tree):
+        if isinstance(node, (ast.FunctionDef, ast.ClassDef, ast.AsyncFunctionDef)):
+            bound.add(node.name)
+        elif isinstance(node, ast.arg):
+            bound.add(node.arg)
+        elif isinstance(node, ast.Name) and isinstance(node.ctx, (ast.Store, ast.Del)):
+            bound.add(node.id)
+        elif isinstance(node, (ast.Import, ast.ImportFrom)):
+            bound.update((a.asname or a.name).split(".")[0] for a in node.names)
+        elif isinstance(node, ast.ExceptHandler) and node.name:
+            bound.add(node.name)
+    loaded = {n.id for n in ast.walk(tree) if isinstance(n, ast.Name) and isinstance(n.ctx, ast.Load)}
+    assert loaded <= bound, sorted(loaded - bound)
+
+
+def test_clock_reading_never_raises_without_a_gpu():
+    calls = []
+    r = bench.ClockUnderLoad().measure(lambda: calls.append(1), max_s=0.1)
+    assert "median_mhz" in r
+    if r["median_mhz"] is None:
+        assert r.get("error")
