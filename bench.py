@@ -242,8 +242,11 @@ class ClockUnderLoad:
 def time_steps(call, steps: int, stream) -> dict:
     """The K timed steps: one event before the first launch and one after the last,
     with a synchronize on both sides (ms_per_step = elapsed / K, nothing between the
-    launches).  Then a separate loop of K launches, each between its own pair of
-    events, for per-launch statistics (the kernel's own duration for the roofline)."""
+    launches).  Each step is one call of the entry point, so ms_per_step is also the
+    average launch duration the roofline divides by.  Then a separate loop of K
+    launches, each between its own pair of events, for the spread of launch times
+    (reported only: the event records between launches add a few microseconds to
+    each one)."""
     import torch
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -372,10 +375,10 @@ def bench_softmax(args, w):
     warm = warm_up(lambda: eta.softmax_rows(x, y, stream=stream), args.warmup)
     t = time_steps(lambda: eta.softmax_rows(x, y, stream=stream), args.steps, stream)
     sclk = None if args.no_clock else ClockUnderLoad().measure(lambda: eta.softmax_rows(x, y, stream=stream))
-    ms_per_step, launch_ms = t["ms_per_step"], t["launch_ms"]
+    ms_per_step = t["ms_per_step"]
     nbytes = w.algorithmic_bytes()
     value = nbytes / (ms_per_step * 1e-3) / 1e9
-    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    achieved = nbytes / (ms_per_step * 1e-3) / 1e9
     kernel = "softmax_row_tiled_kernel" if w.cols > 65536 else "softmax_row_kernel"
     line = {
         "metric": METRIC_SOFTMAX,
@@ -448,10 +451,10 @@ def bench_gemm(args, w):
     warm = warm_up(call, args.warmup)
     t = time_steps(call, args.steps, stream)
     sclk = None if args.no_clock else ClockUnderLoad().measure(call)
-    ms_per_step, launch_ms = t["ms_per_step"], t["launch_ms"]
+    ms_per_step = t["ms_per_step"]
     flops = w.flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (launch_ms * 1e-3) / 1e12
+    achieved = flops / (ms_per_step * 1e-3) / 1e12
     line = {
         "metric": METRIC_GEMM,
         "value": round(value, 2),
@@ -501,10 +504,10 @@ def bench_backward(args, w, causal):
     warm = warm_up(call, args.warmup)
     t = time_steps(call, args.steps, stream)
     sclk = None if args.no_clock else ClockUnderLoad().measure(call)
-    ms_per_step, launch_ms = t["ms_per_step"], t["launch_ms"]
+    ms_per_step = t["ms_per_step"]
     flops = 2.5 * w.flops(causal)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (launch_ms * 1e-3) / 1e12
+    achieved = flops / (ms_per_step * 1e-3) / 1e12
     line = {
         "metric": METRIC_BWD,
         "value": round(value, 2),
@@ -559,11 +562,11 @@ def bench_merge(args, w, G):
     warm = warm_up(call, args.warmup)
     t = time_steps(call, args.steps, stream)
     sclk = None if args.no_clock else ClockUnderLoad().measure(call)
-    ms_per_step, launch_ms = t["ms_per_step"], t["launch_ms"]
+    ms_per_step = t["ms_per_step"]
     rows = w.B * w.H * w.N
     nbytes = G * rows * (w.d * 2 + 4) + rows * (w.d * 2 + 4)
     value = nbytes / (ms_per_step * 1e-3) / 1e9
-    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    achieved = nbytes / (ms_per_step * 1e-3) / 1e9
     line = {
         "metric": METRIC_MERGE, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "warmup_detail": warm, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
@@ -707,10 +710,10 @@ def main():
     warm = warm_up(call, args.warmup)
     t = time_steps(call, args.steps, stream)
     sclk = None if args.no_clock else ClockUnderLoad().measure(call)
-    ms_per_step, launch_ms = t["ms_per_step"], t["launch_ms"]
+    ms_per_step = t["ms_per_step"]
     flops = launch_flops(w, causal, args.window)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = flops / (launch_ms * 1e-3) / 1e12
+    achieved = flops / (ms_per_step * 1e-3) / 1e12
 
     line = {
         "metric": METRIC if args.window <= 0 else METRIC_WINDOW,
@@ -732,8 +735,9 @@ def main():
                    **launch_stats(t), "sclk": sclk,
                    "pct_of_peak_at_sclk": (round(100 * achieved / (MFMA_PEAK_TFLOPS * sclk["median_mhz"] / 2400.0), 2)
                                            if sclk and sclk.get("median_mhz") else None),
-                   "timing": "ms_per_step: one event pair around the K timed steps; launch_ms_*: a second loop of K "
-                             "launches, each between its own events"},
+                   "timing": "ms_per_step: one event pair around the K timed steps (also the roofline's launch "
+                             "duration); launch_ms_*: a second loop of K launches, each between its own events "
+                             "(those records add a few microseconds per launch)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(w.name, causal, args.window),
