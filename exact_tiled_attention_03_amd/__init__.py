@@ -53,6 +53,12 @@ def load_library():
                                     ctypes.c_float, ctypes.c_int, ctypes.c_void_p]
     lib.attn_fwd_schedule.restype = ctypes.c_int
     lib.attn_fwd_schedule.argtypes = [ctypes.c_int] * 5
+    lib.attn_fwd_ws.restype = ctypes.c_int
+    lib.attn_fwd_ws.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.attn_fwd_workspace_bytes.restype = ctypes.c_longlong
+    lib.attn_fwd_workspace_bytes.argtypes = [ctypes.c_int] * 5
     lib.attn_bwd.restype = ctypes.c_int
     lib.attn_bwd.argtypes = [ctypes.c_void_p] * 10 + [ctypes.c_int] * 5 + [ctypes.c_float, ctypes.c_int,
                                                                            ctypes.c_void_p]
@@ -105,15 +111,8 @@ def _stream_handle(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def attn_fwd(q, k, v, out, lse, causal: bool, scale: float, stream=None, window: int = 0) -> None:
-    """Enqueue the forward pass on `stream` (default: torch's current stream).
-
-    q, k, v, out: contiguous [B, H, N, d] float16/bfloat16 tensors on the GPU.
-    lse: contiguous [B, H, N] float32 tensor on the GPU, or None.
-    window: 0 for full attention (attn_fwd), W >= 1 for the sliding window of
-    attn_fwd_window (key j kept only if i - W < j, and j < i + W when not causal).
-    Raises AttnError with the library's status on rejected arguments."""
-    lib = load_library()
+def _check_attn_tensors(q, k, v, out, lse):
+    """Shapes, dtypes and placement of attn_fwd's tensors; returns (B, H, N, d)."""
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d]")
     B, H, N, d = q.shape
@@ -132,6 +131,19 @@ def attn_fwd(q, k, v, out, lse, causal: bool, scale: float, stream=None, window:
         import torch
         if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N):
             raise ValueError("lse must be float32 [B, H, N]")
+    return B, H, N, d
+
+
+def attn_fwd(q, k, v, out, lse, causal: bool, scale: float, stream=None, window: int = 0) -> None:
+    """Enqueue the forward pass on `stream` (default: torch's current stream).
+
+    q, k, v, out: contiguous [B, H, N, d] float16/bfloat16 tensors on the GPU.
+    lse: contiguous [B, H, N] float32 tensor on the GPU, or None.
+    window: 0 for full attention (attn_fwd), W >= 1 for the sliding window of
+    attn_fwd_window (key j kept only if i - W < j, and j < i + W when not causal).
+    Raises AttnError with the library's status on rejected arguments."""
+    lib = load_library()
+    B, H, N, d = _check_attn_tensors(q, k, v, out, lse)
     lse_ptr = lse.data_ptr() if lse is not None else None
     if window:
         st = lib.attn_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
@@ -140,6 +152,32 @@ def attn_fwd(q, k, v, out, lse, causal: bool, scale: float, stream=None, window:
     else:
         st = lib.attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse_ptr,
                           B, H, N, d, int(bool(causal)), float(scale), _dtype_code(q), _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, attn_status_string(st))
+
+
+def attn_fwd_workspace_bytes(B: int, H: int, N: int, d: int, causal: bool) -> int:
+    """Workspace bytes attn_fwd_ws uses for this shape on the current device (0: no split)."""
+    r = load_library().attn_fwd_workspace_bytes(int(B), int(H), int(N), int(d), int(bool(causal)))
+    if r < 0:
+        raise AttnError(-r, attn_status_string(-r))
+    return r
+
+
+def attn_fwd_ws(q, k, v, out, lse, causal: bool, scale: float, workspace, stream=None) -> None:
+    """attn_fwd_ws: attn_fwd that may cut the last query tiles into key ranges run
+    on otherwise idle CUs, with partial results in `workspace` (a contiguous GPU
+    tensor of at least attn_fwd_workspace_bytes bytes, or None for attn_fwd)."""
+    lib = load_library()
+    B, H, N, d = _check_attn_tensors(q, k, v, out, lse)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    st = lib.attn_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                         lse.data_ptr() if lse is not None else None, B, H, N, d, int(bool(causal)), float(scale),
+                         _dtype_code(q), ws_ptr, ws_bytes, _stream_handle(stream))
     if st != ATTN_OK:
         raise AttnError(st, attn_status_string(st))
 

@@ -43,6 +43,7 @@
 // half and the matrix half of a key tile (see the kernel).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cfloat>
 #include <cmath>
@@ -51,6 +52,7 @@
 #include <type_traits>
 
 #include "attn.h"
+#include "attn_bwd.h"
 #include "launch.h"
 #include "lds_load.h"
 
@@ -113,6 +115,18 @@ struct FwdArgs {
     float c;           // |scale| * log2(e), > 0
     unsigned qsign;    // 0x80008000 when scale < 0 (Q negated exactly), else 0
     int window;        // 0: none; W in [1, N): key j kept for query i only if i - W < j (and j < i + W if not causal)
+    // Key-range parts (the PARTS kernel only): work units 0 .. nwhole-1 are whole
+    // query tiles; the other nleft tiles (the last ones in (head, tile) order,
+    // whose rows row0 .. row0+rows-1 of the [BH*N] row space are contiguous)
+    // are each cut into nparts key ranges, part p of them written to
+    // o_parts[p][row - row0][:] (normalised by its own sum) and lse_parts[p][row - row0].
+    int nwhole;        // whole work units (ngroups * BH without parts)
+    int nleft;
+    int nparts;
+    long long row0;
+    long long rows;
+    uint16_t* o_parts;
+    float* lse_parts;
 };
 
 // x combined with the value in the lane 32 positions away (the other half of
@@ -203,8 +217,7 @@ __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)"
 // Work-group id -> (head, group): ids are dealt round-robin over the 8 XCDs,
 // so XCD x runs ids x, x+8, ...; the remap gives each XCD a contiguous range
 // of (head, group) indices.
-__device__ __forceinline__ void map_workgroup(const FwdArgs& a, int L, int& bh, int& grp) {
-    const int T = a.ngroups * a.BH;
+__device__ __forceinline__ void map_workgroup(const FwdArgs& a, int L, int T, int& bh, int& grp) {
     const int xcd = L & 7;
     const int vidx = xcd * (T >> 3) + min(xcd, T & 7) + (L >> 3);
     bh = vidx / a.ngroups;
@@ -456,13 +469,24 @@ struct Wave {
         }
     }
 
-    // O = acc / l rounded to the input type; lse = ln2 * (m + log2 l).  The wave's
-    // 32 x D block goes through its own slice of LDS (32 rows of ROWB bytes, the
-    // 16-byte chunk c of row r at c ^ (r % CPRP)) so that the global stores are
-    // whole rows: each store instruction writes 64/CPRP consecutive rows.  Only
-    // called when no wave reads the K/V stages and no tile load is in flight
-    // (after the last barrier of a query tile, before the next one's first).
-    __device__ __forceinline__ void finish(const FwdArgs& a, int bh) {
+    // O = acc / l rounded to the input type; lse = ln2 * (m + log2 l), written
+    // to out / lse (may be null) as rows row .. row+31 of a [rows, D] array.  The
+    // wave's 32 x D block goes through its own slice of LDS (32 rows of ROWB
+    // bytes, the 16-byte chunk c of row r at c ^ (r % CPRP)) so that the global
+    // stores are whole rows: each store instruction writes 64/CPRP consecutive
+    // rows.  Only called when no wave reads the K/V stages and no tile load is
+    // in flight (after the last barrier of a query tile, before the next one's
+    // first).
+    __device__ __forceinline__ void finish(const FwdArgs& a, int bh) { store(a.o, a.lse, (size_t)bh * N + qw0); }
+
+    // the result of key-range part `part` of a query tile: rows past row0 in
+    // the part's slice of the workspace
+    __device__ __forceinline__ void finish_part(const FwdArgs& a, int bh, int part) {
+        store(a.o_parts + (size_t)part * (size_t)a.rows * D, a.lse_parts + (size_t)part * (size_t)a.rows,
+              (size_t)bh * N + qw0 - (size_t)a.row0);
+    }
+
+    __device__ __forceinline__ void store(uint16_t* out, float* lse, size_t row) {
         if (qw0 >= N) return;
         const float ltot = pair_sum(l);
         const float inv = 1.0f / ltot;   // rows past N are never stored
@@ -487,7 +511,7 @@ struct Wave {
             }
         constexpr int RPR = 64 / C::CPRP;                     // rows per store round
         const int rr = ln / C::CPRP, c = ln % C::CPRP;
-        uint16_t* obase = a.o + ((size_t)bh * N + qw0) * D;
+        uint16_t* obase = out + row * D;
         // every round's row read first, then the stores back to back
         u32x4_t v[32 / RPR];
 #pragma unroll
@@ -505,7 +529,7 @@ struct Wave {
                 __builtin_nontemporal_store(v[k], reinterpret_cast<u32x4_t*>(obase + (unsigned)(r * D + 8 * c)));
             }
         }
-        if (a.lse != nullptr && hf == 0 && qi < N) a.lse[(size_t)bh * N + qi] = (m + __builtin_amdgcn_logf(ltot)) * kLn2;
+        if (lse != nullptr && hf == 0 && qi < N) lse[row + n] = (m + __builtin_amdgcn_logf(ltot)) * kLn2;
     }
 };
 
@@ -524,11 +548,17 @@ template <int WAVES> constexpr int fwd_stages() { return fwd_ping<WAVES>() ? 3 :
 // results of a row are merged through LDS at the end of the item.  Used for
 // short problems where one 256-query work-group per CU would leave CUs idle
 // and the 4-wave grid would leave them with one wave per SIMD.
-template <int D, int DT, bool CAUSAL, int WAVES, bool WIN, bool SPLIT = false>
+//
+// PARTS (8 waves, no mask, no window, no SPLIT): besides whole query tiles the
+// work units include key-range parts of the last query tiles (see FwdArgs),
+// so that an incomplete last round of the resident work-groups is spread over
+// all of them; attn_lse_merge combines the parts afterwards.
+template <int D, int DT, bool CAUSAL, int WAVES, bool WIN, bool SPLIT = false, bool PARTS = false>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
     static_assert(!SPLIT || (WAVES == 8 && !WIN), "the key split is a form of the 8-wave schedule without a window");
+    static_assert(!PARTS || (WAVES == 8 && !WIN && !SPLIT && !CAUSAL), "key-range parts: 8-wave unmasked schedule");
     constexpr int STAGES = fwd_stages<WAVES>();
     constexpr int SUBS = SPLIT ? 2 : 1;
     using C = Cfg<D, WAVES, STAGES, SUBS>;
@@ -547,11 +577,21 @@ void attn_fwd_kernel(FwdArgs a) {
     // Work units (a query tile, or a causal pair of them) blockIdx.x,
     // blockIdx.x + gridDim.x, ...: the grid is either one work-group per unit
     // or, for the 8-wave kernel, a multiple of 8 work-groups that stay resident
-    // (a unit keeps its XCD since gridDim.x % 8 == 0).
+    // (a unit keeps its XCD since gridDim.x % 8 == 0).  With PARTS, units past
+    // the whole ones are the parts of the remaining tiles, tile by tile.
     bool first = true;
-    for (int unit = blockIdx.x; unit < a.ngroups * a.BH; unit += gridDim.x) {
-    int bh, grp;
-    map_workgroup(a, unit, bh, grp);
+    const int nunits = PARTS ? a.nwhole + a.nleft * a.nparts : a.nwhole;
+    for (int unit = blockIdx.x; unit < nunits; unit += gridDim.x) {
+    int bh, grp, part = -1;
+    if (!PARTS || unit < a.nwhole) {
+        map_workgroup(a, unit, a.nwhole, bh, grp);
+    } else {
+        const int u = unit - a.nwhole, left = u / a.nparts;
+        part = u - left * a.nparts;
+        const int g = a.nwhole + left;
+        bh = g / a.ngroups;
+        grp = g - bh * a.ngroups;
+    }
     const int nitems = CAUSAL && grp != a.nqt - 1 - grp ? 2 : 1;
     for (int item = 0; item < nitems; ++item, first = false) {
         const int qt = CAUSAL ? (item == 0 ? a.nqt - 1 - grp : grp) : grp;
@@ -562,8 +602,13 @@ void attn_fwd_kernel(FwdArgs a) {
         // from the first query's band start
         const int win = WIN ? a.window : 0;
         const int kend = CAUSAL ? min(a.N, q0 + BMQ) : (win > 0 ? min(a.N, q0 + BMQ - 1 + win) : a.N);
-        const int nt = (kend + C::BN - 1) / C::BN;
-        const int jlo = win > 0 ? max(0, q0 - win + 1) / C::BN : 0;
+        int nt = (kend + C::BN - 1) / C::BN;
+        int jlo = win > 0 ? max(0, q0 - win + 1) / C::BN : 0;
+        if (PARTS && part >= 0) {                          // key tiles of this part: an even share
+            const int ti = nt - jlo;
+            nt = jlo + ti * (part + 1) / a.nparts;
+            jlo = jlo + ti * part / a.nparts;
+        }
 
         if constexpr (fwd_ping<WAVES>()) {
             // Two groups of four waves, one wave of each on every SIMD.  Every
@@ -712,6 +757,8 @@ void attn_fwd_kernel(FwdArgs a) {
                     w.m = mm;
                     w.finish(a, bh);
                 }
+            } else if (PARTS && part >= 0) {
+                w.finish_part(a, bh, part);
             } else {
                 w.finish(a, bh);
             }
@@ -802,9 +849,59 @@ hipError_t launch_waves(FwdArgs a, hipStream_t stream, int cus) {
     a.nqt = (int)nqt;
     a.ngroups = CAUSAL ? (int)((nqt + 1) / 2) : (int)nqt;
     const unsigned units = (unsigned)a.ngroups * (unsigned)a.BH;
+    a.nwhole = (int)units;
     unsigned grid = units;
     if (fwd_ping<WAVES>() && cus >= 8 && units > (unsigned)cus) grid = (unsigned)cus & ~7u;
     return launch_kernel(attn_fwd_kernel<D, DT, CAUSAL, WAVES, WIN, SPLIT>, dim3(grid), dim3(64 * WAVES), stream, a);
+}
+
+// Key-range parts (attn_fwd_ws).  With I query tiles of 256 rows over S
+// resident 8-wave work-groups, a last round of r = I mod S tiles would leave
+// S - r CUs idle for a whole tile's time.  Instead the last r tiles (in
+// (head, tile) order, so their rows are one contiguous range) are each cut
+// into P = min(S / r, key tiles / 2) key ranges that run as one short round on
+// all work-groups, and attn_lse_merge combines the P partial results.  Only
+// without a mask: a causal problem already pairs its tiles to equal work.
+struct PartPlan {
+    int nwhole = 0, nleft = 0, nparts = 0;
+    long long row0 = 0, rows = 0;
+    size_t o_bytes = 0, lse_bytes = 0, tmp_bytes = 0;   // workspace: O parts, lse parts, merged lse
+    size_t total() const { return o_bytes + lse_bytes + tmp_bytes; }
+};
+
+constexpr long long kPartMinTiles = 2;   // key tiles per part at least
+
+PartPlan plan_parts(long long bh, long long N, int d, int causal, int cus) {
+    PartPlan p;
+    if (causal || cus < 8) return p;
+    const long long S = cus & ~7, nqt = (N + 255) / 256, items = nqt * bh;
+    const long long r = items % S;
+    if (r == 0) return p;
+    const long long P = std::min(S / r, ((N + 63) / 64) / kPartMinTiles);
+    if (P < 2) return p;
+    p.nparts = (int)P;
+    p.nleft = (int)r;
+    p.nwhole = (int)(items - r);
+    p.row0 = (p.nwhole / nqt) * N + (p.nwhole % nqt) * 256;
+    p.rows = bh * N - p.row0;
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    p.o_bytes = up((size_t)P * (size_t)p.rows * (size_t)d * 2u);
+    p.lse_bytes = up((size_t)P * (size_t)p.rows * 4u);
+    p.tmp_bytes = up((size_t)p.rows * 4u);
+    return p;
+}
+
+template <int D, int DT>
+hipError_t launch_parts(FwdArgs a, const PartPlan& p, hipStream_t stream, int cus) {
+    a.nqt = (a.N + 255) / 256;
+    a.ngroups = a.nqt;
+    a.nwhole = p.nwhole;
+    a.nleft = p.nleft;
+    a.nparts = p.nparts;
+    a.row0 = p.row0;
+    a.rows = p.rows;
+    const unsigned grid = (unsigned)cus & ~7u;
+    return launch_kernel(attn_fwd_kernel<D, DT, false, 8, false, false, true>, dim3(grid), dim3(512), stream, a);
 }
 
 template <int D, int DT, bool CAUSAL>
@@ -879,8 +976,10 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 namespace {
 
-int fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int N, int d, int causal,
-        int window, float scale, int dtype, void* stream) {
+// Argument checks of every forward entry point (nothing touches the device
+// before they pass) and the kernel arguments they imply.
+int prepare(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int N, int d,
+            int causal, int window, float scale, int dtype, FwdArgs& a, int& cus) {
     if (!q || !k || !v || !out) return ATTN_ERR_NULL;
     if (B < 1 || H < 1 || N < 1) return ATTN_ERR_SHAPE;
     if (d != 64 && d != 80 && d != 128) return ATTN_ERR_HEAD_DIM;
@@ -903,11 +1002,10 @@ int fwd(const void* q, const void* k, const void* v, void* out, float* lse, int 
                 overlaps(lse, lse_bytes, v, tensor_bytes) || overlaps(lse, lse_bytes, out, tensor_bytes)))
         return ATTN_ERR_ALIAS;
 
-    int cus = 0;
     const int dev_status = check_device(&cus);
     if (dev_status != ATTN_OK) return dev_status;
 
-    FwdArgs a;
+    a = FwdArgs{};
     a.q = static_cast<const u32x4_t*>(q);
     a.k = static_cast<const u32x4_t*>(k);
     a.v = static_cast<const u32x4_t*>(v);
@@ -915,14 +1013,22 @@ int fwd(const void* q, const void* k, const void* v, void* out, float* lse, int 
     a.lse = lse;
     a.N = N;
     a.BH = (int)bh;
-    a.nqt = 0;       // set per kernel by launch()
+    a.nqt = 0;       // set per kernel by the launcher
     a.ngroups = 0;
     // c must be > 0 so that masked scores (-inf) map to -inf; scale == 0 uses the
     // smallest normal float, which makes every exponent round to exactly 0
     a.c = scale == 0.f ? FLT_MIN : std::fabs(scale) * kLog2e;
     a.qsign = std::signbit(scale) && scale != 0.f ? 0x80008000u : 0u;
     a.window = window >= N ? 0 : window;   // a band of N or more keeps every key the mask allows
+    return ATTN_OK;
+}
 
+int fwd(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int N, int d, int causal,
+        int window, float scale, int dtype, void* stream) {
+    FwdArgs a;
+    int cus = 0;
+    const int st = prepare(q, k, v, out, lse, B, H, N, d, causal, window, scale, dtype, a, cus);
+    if (st != ATTN_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
     switch (d) {
@@ -931,6 +1037,45 @@ int fwd(const void* q, const void* k, const void* v, void* out, float* lse, int 
         default: err = dispatch_dtype<128>(a, dtype, causal, s, cus); break;
     }
     return err == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+template <int D>
+hipError_t dispatch_parts(const FwdArgs& a, const PartPlan& p, int dtype, hipStream_t s, int cus) {
+    return dtype == ATTN_BF16 ? launch_parts<D, ATTN_BF16>(a, p, s, cus) : launch_parts<D, ATTN_F16>(a, p, s, cus);
+}
+
+int fwd_ws(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int N, int d,
+           int causal, float scale, int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    FwdArgs a;
+    int cus = 0;
+    const int st = prepare(q, k, v, out, lse, B, H, N, d, causal, 0, scale, dtype, a, cus);
+    if (st != ATTN_OK) return st;
+    const PartPlan p = plan_parts(a.BH, N, d, causal, cus);
+    if (workspace == nullptr || p.nparts == 0) return fwd(q, k, v, out, lse, B, H, N, d, causal, 0, scale, dtype, stream);
+    if (workspace_bytes < p.total()) return ATTN_ERR_WORKSPACE;
+    if ((uintptr_t)workspace & 255u) return ATTN_ERR_ALIGN;
+    const size_t tensor_bytes = (size_t)a.BH * (size_t)N * (size_t)d * 2u;
+    const size_t lse_bytes = (size_t)a.BH * (size_t)N * 4u;
+    if (overlaps(workspace, p.total(), q, tensor_bytes) || overlaps(workspace, p.total(), k, tensor_bytes) ||
+        overlaps(workspace, p.total(), v, tensor_bytes) || overlaps(workspace, p.total(), out, tensor_bytes) ||
+        (lse && overlaps(workspace, p.total(), lse, lse_bytes)))
+        return ATTN_ERR_ALIAS;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    a.o_parts = reinterpret_cast<uint16_t*>(ws);
+    a.lse_parts = reinterpret_cast<float*>(ws + p.o_bytes);
+    float* lse_merged = lse ? lse + p.row0 : reinterpret_cast<float*>(ws + p.o_bytes + p.lse_bytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    switch (d) {
+        case 64: err = dispatch_parts<64>(a, p, dtype, s, cus); break;
+        case 80: err = dispatch_parts<80>(a, p, dtype, s, cus); break;
+        default: err = dispatch_parts<128>(a, p, dtype, s, cus); break;
+    }
+    if (err != hipSuccess) return ATTN_ERR_LAUNCH;
+    // the rows of the cut tiles: O and lse from their parts, on the same stream
+    const int mst = attn_lse_merge(a.o_parts, a.lse_parts, p.nparts, static_cast<uint16_t*>(out) + p.row0 * d,
+                                   lse_merged, p.rows, d, dtype, stream);
+    return mst == ATTN_OK ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
 
 }  // namespace
@@ -944,6 +1089,21 @@ extern "C" int attn_fwd_window(const void* q, const void* k, const void* v, void
                                int B, int H, int N, int d, int causal, int window, float scale, int dtype,
                                void* stream) {
     return fwd(q, k, v, out, lse, B, H, N, d, causal, window, scale, dtype, stream);
+}
+
+extern "C" int attn_fwd_ws(const void* q, const void* k, const void* v, void* out, float* lse, int B, int H, int N,
+                           int d, int causal, float scale, int dtype, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    return fwd_ws(q, k, v, out, lse, B, H, N, d, causal, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+extern "C" long long attn_fwd_workspace_bytes(int B, int H, int N, int d, int causal) {
+    const int st = check_shape(B, H, N, d, causal);
+    if (st != ATTN_OK) return -st;
+    int cus = 0;
+    const int dev_status = check_device(&cus);
+    if (dev_status != ATTN_OK) return -dev_status;
+    return (long long)plan_parts((long long)B * H, N, d, causal, cus).total();
 }
 
 extern "C" int attn_fwd_schedule(int B, int H, int N, int d, int causal) {

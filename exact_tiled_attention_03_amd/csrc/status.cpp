@@ -25,6 +25,7 @@ extern "C" const char* attn_status_string(int status) {
         case ATTN_ERR_ALIAS: return "an output overlaps an input or another output";
         case ATTN_ERR_WINDOW: return "window must be >= 0";
         case ATTN_ERR_LAYOUT: return "b_layout or act is not a listed value";
+        case ATTN_ERR_WORKSPACE: return "workspace smaller than attn_fwd_workspace_bytes for this shape";
         default: return "unknown status";
     }
 }

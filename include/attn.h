@@ -22,6 +22,8 @@
 #ifndef ETA_ATTN_H
 #define ETA_ATTN_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -50,7 +52,8 @@ typedef enum {
     ATTN_ERR_CAUSAL = 9,    /* causal is neither 0 nor 1 */
     ATTN_ERR_ALIAS = 10,    /* out or lse overlaps q, k, v, or each other */
     ATTN_ERR_WINDOW = 11,   /* window is negative */
-    ATTN_ERR_LAYOUT = 12    /* gemm_bias_act: b_layout or act is not a listed value */
+    ATTN_ERR_LAYOUT = 12,   /* gemm_bias_act: b_layout or act is not a listed value */
+    ATTN_ERR_WORKSPACE = 13 /* attn_fwd_ws: workspace smaller than attn_fwd_workspace_bytes */
 } attn_status;
 
 /*
@@ -113,6 +116,49 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, float* lse,
 int attn_fwd_window(const void* q, const void* k, const void* v, void* out, float* lse,
                     int B, int H, int N, int d, int causal, int window, float scale, int dtype,
                     void* stream);
+
+/*
+ * attn_fwd_ws -- attn_fwd with a caller workspace, used to fill the GPU when
+ * the query tiles leave an incomplete last round.
+ *
+ * Query tile i and head h are one unit of work in the method of "Triton in
+ * depth" section 3.3; on a GPU that runs S work-groups at a time, a last round
+ * of r < S units keeps the other S - r compute units idle for a whole unit's
+ * time.  For causal = 0, when 0 < r <= S/2 for the 256-query tiles, the last r
+ * tiles are instead each cut into P = min(S / r, key tiles / 2) key ranges
+ * (64 keys per key tile) that run in one short round, and every row of those
+ * tiles is combined from its P partial results exactly as attn_lse_merge
+ * (attn_bwd.h) documents: each partial is computed like attn_fwd over its key
+ * range, its O rounded to `dtype`.  The result equals attn_fwd's up to that
+ * extra rounding of the partial O (within a unit in the last place of `dtype`
+ * of the exact row, typically).
+ *
+ *   workspace       : device pointer, 256-byte aligned, or NULL.  NULL, or a
+ *                     shape that needs no split (attn_fwd_workspace_bytes returns
+ *                     0), gives exactly attn_fwd.  Its contents on entry do not
+ *                     matter; on return they are unspecified.
+ *   workspace_bytes : its size; at least attn_fwd_workspace_bytes(B, H, N, d,
+ *                     causal) when workspace is not NULL.
+ *
+ * Other arguments, layout, arithmetic and the remaining errors as attn_fwd (no
+ * window).  Two kernels are enqueued on `stream` (the forward, then the merge).
+ * Errors: ATTN_ERR_WORKSPACE when workspace is not NULL, a split is used and
+ * workspace_bytes is too small; ATTN_ERR_ALIGN when workspace is not 256-byte
+ * aligned; ATTN_ERR_ALIAS when it overlaps q, k, v, out or lse.  The caller owns
+ * the workspace; calls that may run at the same time need workspaces of their own.
+ */
+int attn_fwd_ws(const void* q, const void* k, const void* v, void* out, float* lse,
+                int B, int H, int N, int d, int causal, float scale, int dtype,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_fwd_workspace_bytes -- workspace attn_fwd_ws uses for a shape on the
+ * current device (its compute-unit count sets S): 0 when it would not split,
+ * else P x rows x (2 d + 4) + rows x 4 bytes (rows = those of the cut tiles),
+ * each area rounded up to 256 bytes.  A negative attn_status for arguments
+ * attn_fwd would reject by shape, or -ATTN_ERR_DEVICE.
+ */
+long long attn_fwd_workspace_bytes(int B, int H, int N, int d, int causal);
 
 /*
  * attn_fwd_schedule -- which kernel schedule attn_fwd uses for a shape

@@ -39,10 +39,11 @@ def declared_enum(name_prefix, header=HEADER):
 
 
 def test_header_declares_entry_points():
-    assert declared_functions([HEADER]) == ["attn_fwd", "attn_fwd_schedule", "attn_fwd_window", "attn_status_string"]
+    assert declared_functions([HEADER]) == ["attn_fwd", "attn_fwd_schedule", "attn_fwd_window", "attn_fwd_workspace_bytes",
+                                            "attn_fwd_ws", "attn_status_string"]
     assert declared_functions() == ["attn_bwd", "attn_bwd_noalloc", "attn_fwd", "attn_fwd_schedule",
-                                    "attn_fwd_window", "attn_lse_merge", "attn_status_string", "gemm_bias_act",
-                                    "softmax_rows"]
+                                    "attn_fwd_window", "attn_fwd_workspace_bytes", "attn_fwd_ws", "attn_lse_merge",
+                                    "attn_status_string", "gemm_bias_act", "softmax_rows"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -113,6 +114,43 @@ def test_window_valid_arguments_reach_the_device_check(lib):
         pytest.skip("device check refuses only where no gfx950 is current")
     for w in (0, 1, 7, 16, 10**9):
         assert call_window(lib, w) == 7
+
+
+WS = A + 8 * SZ      # fake workspace, 256-byte aligned, disjoint from the other fake buffers
+
+
+def call_ws(lib, ws=WS, ws_bytes=1 << 30, **kw):
+    a = dict(q=A, k=A + SZ, v=A + 2 * SZ, out=A + 3 * SZ, lse=A + 4 * SZ, B=1, H=1, N=16, d=64, causal=0,
+             scale=0.125, dtype=0)
+    a.update(kw)
+    return lib.attn_fwd_ws(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["N"], a["d"], a["causal"],
+                           a["scale"], a["dtype"], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), 1), (dict(out=None), 1), (dict(B=0), 2), (dict(N=0), 2), (dict(d=96), 3),
+    (dict(dtype=2), 4), (dict(scale=math.nan), 5), (dict(q=A + 8), 6), (dict(causal=2), 9),
+    (dict(out=A + 64), 10), (dict(lse=A + 2 * SZ), 10),
+])
+def test_ws_argument_validation(lib, kw, code):
+    """attn_fwd_ws checks the arguments attn_fwd checks before any device query."""
+    assert call_ws(lib, **kw) == code, eta.attn_status_string(code)
+    assert call_ws(lib, ws=None, ws_bytes=0, **kw) == code
+
+
+def test_ws_valid_arguments_reach_the_device_check(lib):
+    if gpu_available():
+        pytest.skip("device check refuses only where no gfx950 is current")
+    for kw in (dict(), dict(causal=1), dict(lse=None), dict(ws=None, ws_bytes=0), dict(ws_bytes=0)):
+        assert call_ws(lib, **kw) == 7
+    assert lib.attn_fwd_workspace_bytes(1, 24, 3000, 80, 0) == -7
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 1, 16, 64, 0), 2), ((1, 1, 0, 64, 0), 2), ((1, 1, 16, 96, 0), 3), ((1, 1, 16, 64, 2), 9),
+])
+def test_workspace_bytes_rejects_bad_shapes(lib, args, code):
+    assert lib.attn_fwd_workspace_bytes(*args) == -code
 
 
 def test_lse_may_be_null_then_device_is_checked(lib):
