@@ -128,6 +128,15 @@ def _pmc_kib_per_dispatch(directory: str, counter: str, kernel_substr: str) -> f
     return statistics.median(vals.values())
 
 
+def _has_kernel(directory: str, kernel_substr: str) -> bool:
+    import csv
+    import glob
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        if any(kernel_substr in r["Kernel_Name"] for r in csv.DictReader(open(f))):
+            return True
+    return False
+
+
 def traffic_summary(attn_fetch, attn_write, copy_fetch, copy_write, workload, causal, window=0,
                     kernel_substr="attn_fwd_kernel", source=KERNEL_SOURCE, key=None):
     """HBM bytes per kernel launch: FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by
@@ -643,6 +652,8 @@ def main():
     ap.add_argument("--backward", action="store_true", help="time attn_bwd on the attention workload")
     ap.add_argument("--merge", type=int, default=0, help="time attn_lse_merge over this many key shards")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--entry", choices=["auto", "attn_fwd"], default="auto",
+                    help="forward entry point: auto uses attn_fwd_ws where it splits the last round")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the clock-under-load window (for profiler runs, which time every dispatch)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -666,6 +677,10 @@ def main():
         elif args.merge > 0:
             traffic_summary(*args.traffic_summary, w.name, None, 0, "lse_merge_kernel", MERGE_SOURCE,
                             key=f"{w.name}-merge{args.merge}")
+        elif _has_kernel(args.traffic_summary[0], "lse_merge_kernel"):
+            # an attn_fwd_ws run: the forward with key-range parts and the merge
+            traffic_summary(*args.traffic_summary, w.name, causal, 0, ("attn_fwd_kernel", "lse_merge_kernel"),
+                            key=traffic_key(w.name, causal) + "-ws")
         else:
             traffic_summary(*args.traffic_summary, w.name, causal, args.window)
         return
@@ -703,9 +718,17 @@ def main():
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    # attn_fwd_ws where it splits a partial last round of query tiles (its
+    # workspace allocated here, outside the timed region), else attn_fwd
+    ws_bytes = 0 if args.window > 0 or args.entry == "attn_fwd" else eta.attn_fwd_workspace_bytes(w.B, w.H, w.N, w.d, causal)
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes > 0 else None
+    entry = "attn_fwd_ws" if workspace is not None else ("attn_fwd_window" if args.window > 0 else "attn_fwd")
 
     def call():
-        eta.attn_fwd(q, k, v, out, lse, causal, w.scale, stream=stream, window=args.window)
+        if workspace is not None:
+            eta.attn_fwd_ws(q, k, v, out, lse, causal, w.scale, workspace, stream=stream)
+        else:
+            eta.attn_fwd(q, k, v, out, lse, causal, w.scale, stream=stream, window=args.window)
 
     warm = warm_up(call, args.warmup)
     t = time_steps(call, args.steps, stream)
@@ -731,7 +754,8 @@ def main():
         "data": "synthetic (seeded iid N(0,1) Q, K, V)",
         "config": {"workload": w.name + (f"-window{args.window}" if args.window > 0 else ""),
                    "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": causal, "window": args.window,
-                   "scale": w.scale, "layout": "[B,H,N,d] contiguous", "pct_of_mfma_peak": round(100 * value / MFMA_PEAK_TFLOPS, 2),
+                   "scale": w.scale, "layout": "[B,H,N,d] contiguous", "entry": entry, "workspace_bytes": ws_bytes,
+                   "pct_of_mfma_peak": round(100 * value / MFMA_PEAK_TFLOPS, 2),
                    **launch_stats(t), "sclk": sclk,
                    "pct_of_peak_at_sclk": (round(100 * achieved / (MFMA_PEAK_TFLOPS * sclk["median_mhz"] / 2400.0), 2)
                                            if sclk and sclk.get("median_mhz") else None),
@@ -740,8 +764,10 @@ def main():
                              "(those records add a few microseconds per launch)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(w.name, causal, args.window),
-                     "kernel": f"attn_fwd_kernel<{w.d},{'bf16' if w.dtype == 'bf16' else 'f16'},{'causal' if causal else 'full'}>",
+                     "traffic": measured_traffic(w.name, causal, args.window,
+                                                 key=(traffic_key(w.name, causal) + "-ws") if workspace is not None else None),
+                     "kernel": f"attn_fwd_kernel<{w.d},{'bf16' if w.dtype == 'bf16' else 'f16'},{'causal' if causal else 'full'}>"
+                               + (" with key-range parts, then lse_merge_kernel (achieved over both)" if workspace is not None else ""),
                      "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": w.algorithmic_bytes()},
         "cpu_baseline": None,
     }

@@ -80,6 +80,10 @@ template <> struct Elem<ATTN_F16> {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
     }
+    // l may be the sum of the probabilities as rounded to this type: its
+    // relative rounding (2^-11) keeps lse within the tolerance (see Wave)
+    static constexpr bool kRoundedSum = true;
+    static constexpr unsigned kOne = 0x3c00u;
     // round-to-nearest-even of two floats, packed low/high
     static __device__ __forceinline__ unsigned pack2(float x, float y) {
         f16x2_t p;
@@ -100,6 +104,8 @@ template <> struct Elem<ATTN_BF16> {
         p[1] = (__bf16)y;
         return __builtin_bit_cast(unsigned, p);
     }
+    static constexpr bool kRoundedSum = false;   // 2^-8 would show in lse
+    static constexpr unsigned kOne = 0x3f80u;
 };
 
 struct FwdArgs {
@@ -231,8 +237,18 @@ struct Wave {
     using C = Cfg<D, WAVES, STAGES, SUBS>;
     using E = Elem<DT>;
     static constexpr int SB = C::SB, KK = C::KK, KSTEPS = C::KSTEPS, DBLK = C::DBLK, CPR = C::CPR;
+    // ONES: the head dim leaves padding in the last 32-row block of O^T (d = 80:
+    // rows 80..95).  Column D of every V row in LDS is set to 1, so O^T row D
+    // accumulates the row sum l of the rounded probabilities with the P.V
+    // MFMAs that run anyway, rescaled with O, instead of one add per score.
+    // Used where it measured faster: the unmasked 8-wave schedule (+2-3% at
+    // d = 80 fp16; -0.9% causal and -4.6% with 4 waves, whose extra LDS writes
+    // and registers cost more than the adds).
+    static constexpr bool ONES = D % 32 != 0 && E::kRoundedSum && WAVES == 8 && !CAUSAL;
+    static constexpr int LDB = D / 32, LREG = 4 * ((D % 32) / 8);   // O^T row D: o[LDB][LREG] of the lanes with hf = 0
 
     int lane, wave, hf, n, N, qw0, qi, W;
+    unsigned onesm;                    // bit it: this lane's slot of load round it holds V column D
     float c;
     unsigned lds0;
     const unsigned char* kbase;
@@ -242,7 +258,7 @@ struct Wave {
     unsigned va[DBLK];                 // per-lane LDS addresses of the P.V A operand
     u32x4_t qf[KSTEPS];                // Q^T fragments (score B operand)
     f32x16_t o[DBLK];                  // O^T accumulator
-    float m, l;                        // reference max (log2 units) and this half's sum
+    float m, l;                        // reference max (log2 units) and this half's sum (not kept with ONES)
 
     // sub: the tile of each stage this wave reads (the key-split schedule's second
     // pair of waves reads the second tile)
@@ -267,6 +283,12 @@ struct Wave {
             const int vc = p ^ (4 * C::vswz(r));
             kvo[it] = kc < CPR ? (unsigned)(r * D * 2 + kc * 16) : 0x80000000u;
             vvo[it] = vc < CPR ? (unsigned)(r * D * 2 + vc * 16) : 0x80000000u;
+        }
+        onesm = 0;
+#pragma unroll
+        for (int it = 0; it < C::IT; ++it) {
+            const int slot = slot_base(it) + lane;
+            if (((slot % C::CPRP) ^ (4 * C::vswz(slot / C::CPRP))) == CPR) onesm |= 1u << it;
         }
         {
             const int r = kperm(n);
@@ -311,6 +333,22 @@ struct Wave {
 #pragma unroll
         for (int it = 0; it < C::IT; ++it)
             load_lds16(desc, is_v ? vvo[it] : kvo[it], 0, region + (unsigned)(slot_base(it) * 16));
+    }
+
+    // ONES: V column D = 1 (and D+1 .. D+7 = 0) in the rows this wave's loads of
+    // stage ST just filled; the loads write zeros there (the chunk is past the
+    // head dim), so this runs after they have landed, before the barrier that
+    // publishes the tile.
+    template <int ST>
+    __device__ __forceinline__ void ones() const {
+        if constexpr (ONES) {
+            const unsigned region = lds0 + C::VOFF + ST * C::SSTR;
+#pragma unroll
+            for (int it = 0; it < C::IT; ++it)
+                if (onesm & (1u << it))
+                    *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(
+                        (lds_bytes)(size_t)(region + (unsigned)((slot_base(it) + lane) * 16))) = u32x4_t{E::kOne, 0u, 0u, 0u};
+        }
     }
 
     // This wave's 32 Q rows (qw0 ..) into its LDS slice by direct loads: 32 rows of
@@ -399,14 +437,15 @@ struct Wave {
             const float mnew = grow ? mt : m;
             const float alpha = grow ? __builtin_amdgcn_exp2f(m - mnew) : 1.0f;   // 0 when m was -inf
             m = mnew;
-            l *= alpha;
+            if constexpr (!ONES) l *= alpha;
 #pragma unroll
             for (int db = 0; db < DBLK; ++db) o[db] *= alpha;
         }
     }
 
     // P = exp2(c*s - m), rounded to the input type and packed as the B operands
-    // of the P.V k-steps; the fp32 probabilities are added to l
+    // of the P.V k-steps; the fp32 probabilities are added to l (with ONES the
+    // P.V MFMAs sum the rounded ones instead)
     __device__ __forceinline__ void probs(const f32x16_t (&s)[SB], u32x4_t (&pf)[KK]) {
         const float nm = m > kNegInf ? -m : 0.f;
         float part[4] = {0.f, 0.f, 0.f, 0.f};
@@ -416,11 +455,11 @@ struct Wave {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kk >> 1][8 * (kk & 1) + i], c, nm));
-                part[i & 3] += p[i];
+                if constexpr (!ONES) part[i & 3] += p[i];
             }
             pf[kk] = u32x4_t{E::pack2(p[0], p[1]), E::pack2(p[2], p[3]), E::pack2(p[4], p[5]), E::pack2(p[6], p[7])};
         }
-        l += (part[0] + part[1]) + (part[2] + part[3]);
+        if constexpr (!ONES) l += (part[0] + part[1]) + (part[2] + part[3]);
     }
 
     // O^T += V^T P^T for the tile in V stage ST; V^T operand = two transpose
@@ -488,7 +527,9 @@ struct Wave {
 
     __device__ __forceinline__ void store(uint16_t* out, float* lse, size_t row) {
         if (qw0 >= N) return;
-        const float ltot = pair_sum(l);
+        float ltot;
+        if constexpr (ONES) ltot = pair_sum(hf == 0 ? o[LDB][LREG] : 0.f);
+        else ltot = pair_sum(l);
         const float inv = 1.0f / ltot;   // rows past N are never stored
         const unsigned slice = lds0 + (unsigned)(wave * 32 * C::ROWB);
         // the lane's addresses are derived here from an opaque copy of the lane
@@ -559,6 +600,7 @@ void attn_fwd_kernel(FwdArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass only needs the launch stub
     static_assert(!SPLIT || (WAVES == 8 && !WIN), "the key split is a form of the 8-wave schedule without a window");
     static_assert(!PARTS || (WAVES == 8 && !WIN && !SPLIT && !CAUSAL), "key-range parts: 8-wave unmasked schedule");
+    static_assert(!SPLIT || !Wave<D, DT, CAUSAL, WAVES, WIN>::ONES, "the key split merges l, which ONES does not keep");
     constexpr int STAGES = fwd_stages<WAVES>();
     constexpr int SUBS = SPLIT ? 2 : 1;
     using C = Cfg<D, WAVES, STAGES, SUBS>;
@@ -667,16 +709,24 @@ void attn_fwd_kernel(FwdArgs a) {
                 issue_step(true, u + 2, ST2);
             };
             auto tile = [&](auto stage_tag, int u) {
+                constexpr int ST = decltype(stage_tag)::value;
                 if (!g0) issue_tile(stage_tag, u);          // slot 2u+1 starts (group 1)
                 if (has(u)) {
                     w.prepare(s, j0 + u);
                     w.probs(s, pf);
                 }
-                if (g0) wait_loads();                       // slot 2u ends (group 0): tile u+1 landed
+                if (g0) {
+                    wait_loads();                           // slot 2u ends (group 0): tile u+1 landed
+                    if (u == 0) w.template ones<0>();       // (and tile 0, from the prologue)
+                    if (u + 1 < T) w.template ones<(ST + 1) % 3>();
+                }
                 __syncthreads();
                 if (g0) issue_tile(stage_tag, u);           // slot 2u+1 starts (group 0)
                 X(stage_tag, u);
-                if (!g0) wait_loads();                      // slot 2u+2 ends (group 1): tile u+2 landed
+                if (!g0) {
+                    wait_loads();                           // slot 2u+2 ends (group 1): tile u+2 landed
+                    if (u + 2 < T) w.template ones<(ST + 2) % 3>();
+                }
                 __syncthreads();
             };
             // this wave's Q slice: stage 2's K area (waves 0, 1), its V area (2, 3) or
@@ -718,6 +768,8 @@ void attn_fwd_kernel(FwdArgs a) {
             if (has(0)) w.template score<0>(s);
             if (!g0) {
                 wait_loads();
+                w.template ones<0>();
+                if (T > 1) w.template ones<1>();
                 __syncthreads();
             }
             for (int u = 0; u < T; u += 3) {
@@ -787,6 +839,7 @@ void attn_fwd_kernel(FwdArgs a) {
                 w.template pv<ST>(pf);
             }
             wait_loads();
+            if (j + 1 < nt) w.template ones<ST ^ 1>();
             __syncthreads();
         };
         // the Q slices of the 4-wave kernel: stage 1's K area (waves 0, 1) and V
@@ -798,6 +851,7 @@ void attn_fwd_kernel(FwdArgs a) {
         w.issue(false, jlo, 0);
         w.issue(true, jlo, 0);
         wait_loads();
+        w.template ones<0>();
         w.q_read(a, qslice);                               // this wave's own loads: no barrier needed
         __syncthreads();
         for (int j = jlo; j < nt; j += 2) {                 // tile j in stage (j - jlo) & 1
