@@ -133,6 +133,7 @@ struct FwdArgs {
     long long rows;
     uint16_t* o_parts;
     float* lse_parts;
+    int unpaired;      // causal 4-wave grid: one query tile per unit, longest first (see the kernel), instead of pairs
 };
 
 // x combined with the value in the lane 32 positions away (the other half of
@@ -634,9 +635,23 @@ void attn_fwd_kernel(FwdArgs a) {
         bh = g / a.ngroups;
         grp = g - bh * a.ngroups;
     }
-    const int nitems = CAUSAL && grp != a.nqt - 1 - grp ? 2 : 1;
+    int nitems = CAUSAL && grp != a.nqt - 1 - grp ? 2 : 1;
+    int qt_one = -1;
+    if (CAUSAL && WAVES == 4 && !WIN && a.unpaired) {
+        // All U tiles in one round of two work-groups per CU.  With the tiles listed
+        // longest first (tile index descending, heads within a tile index), units
+        // 0 .. U/2-1 take the list from its head and units U/2 .. U-1 from its
+        // tail, so the work-groups dispatched second, which fill the second slot of
+        // each CU in the order the first ones took the first slot, pair a long tile
+        // with a short one on every CU.
+        const int U = a.nqt * a.BH, half = U / 2;
+        const int d = unit < half ? unit : U - 1 - (unit - half);
+        qt_one = a.nqt - 1 - d / a.BH;
+        bh = d % a.BH;
+        nitems = 1;
+    }
     for (int item = 0; item < nitems; ++item, first = false) {
-        const int qt = CAUSAL ? (item == 0 ? a.nqt - 1 - grp : grp) : grp;
+        const int qt = qt_one >= 0 ? qt_one : (CAUSAL ? (item == 0 ? a.nqt - 1 - grp : grp) : grp);
         const int q0 = qt * BMQ;
         // Q rows come through LDS (q_issue / q_read) in every schedule
         w.begin(a, bh, q0 + 32 * (SPLIT ? wave & 3 : wave));
@@ -883,11 +898,18 @@ bool use_wide(long long bh, long long N, int causal) {
 // schedule, +6.6% at B=1 H=16 N=4096 causal and +3.2% at B=2 H=16 N=2048
 // causal, but -4% at N=1024 and -18% at N=128, where the fixed cost of each
 // query tile (first loads, merge, epilogue) outweighs the overlap it gains.
+// Causal problems below 4096 keys whose single query tiles fit one round of
+// two 4-wave work-groups per CU run those unpaired instead (use_unpaired, with
+// the 256 CUs of an MI355X): +1.6 to +8.4% over the key split at N = 2048,
+// -5.9% at N = 4096.
 constexpr long long kSplitBelowGroups = 512;
 constexpr long long kSplitMinN = 2048;
+constexpr long long kUnpairedOverSplitBelowN = 4096;
+constexpr long long kUnpairedMaxTiles = 512;
 
 bool use_split(long long bh, long long N, int d, int causal, int window) {
     if (d != 64 || window > 0 || N < kSplitMinN || use_wide(bh, N, causal)) return false;
+    if (causal && N < kUnpairedOverSplitBelowN && ((N + 127) / 128) * bh <= kUnpairedMaxTiles) return false;
     const long long nqt = (N + 127) / 128;
     return (causal ? (nqt + 1) / 2 : nqt) * bh < kSplitBelowGroups;
 }
@@ -896,12 +918,21 @@ bool use_split(long long bh, long long N, int d, int causal, int window) {
 // leave room for no second one), each looping over work units, so that the
 // grid runs as one round instead of several.
 
+// Causal 4-wave grids whose single query tiles fit one round of two work-groups
+// per CU run them unpaired, longest first (see the kernel): measured +13% at
+// B=4 H=16 N=1024 d=64 and +13-35% on other such shapes, but -11% at twice that
+// many tiles, where the pairs keep every round balanced.
+bool use_unpaired(long long bh, long long N, int causal, int window, int cus) {
+    return causal && window == 0 && cus > 0 && ((N + 127) / 128) * bh <= 2LL * cus;
+}
+
 template <int D, int DT, bool CAUSAL, int WAVES, bool WIN, bool SPLIT = false>
 hipError_t launch_waves(FwdArgs a, hipStream_t stream, int cus) {
     constexpr int BM = SPLIT ? 128 : Cfg<D, WAVES>::BM;
     const long long nqt = ((long long)a.N + BM - 1) / BM;
     a.nqt = (int)nqt;
-    a.ngroups = CAUSAL ? (int)((nqt + 1) / 2) : (int)nqt;
+    a.unpaired = WAVES == 4 && !WIN && use_unpaired(a.BH, a.N, CAUSAL, a.window, cus) ? 1 : 0;
+    a.ngroups = CAUSAL && !a.unpaired ? (int)((nqt + 1) / 2) : (int)nqt;
     const unsigned units = (unsigned)a.ngroups * (unsigned)a.BH;
     a.nwhole = (int)units;
     unsigned grid = units;

@@ -179,6 +179,10 @@ def test_schedule_choice(lib):
     assert eta.attn_fwd_schedule(1, 15, 2047, 64, 0) == 0     # N below 2048
     assert eta.attn_fwd_schedule(1, 4, 4096, 80, 1) == 0      # d = 80 never splits
     assert eta.attn_fwd_schedule(8, 64, 2048, 64, 1) == 1     # wide wins first
+    assert eta.attn_fwd_schedule(1, 16, 2048, 64, 1) == 0     # causal below 4096 keys: 256 unpaired tiles
+    assert eta.attn_fwd_schedule(1, 32, 2048, 64, 1) == 0     # 512 unpaired tiles
+    assert eta.attn_fwd_schedule(1, 33, 2048, 64, 1) == 2     # 528: pairs, and the key split
+    assert eta.attn_fwd_schedule(1, 16, 2048, 64, 0) == 2     # non-causal keeps the split from 2048
     assert eta.attn_fwd_schedule(1, 1, 8, 96, 0) == -3
     assert eta.attn_fwd_schedule(0, 1, 8, 64, 0) == -2
     assert lib.attn_fwd_schedule(1, 1, 8, 64, 3) == -9   # the binding itself coerces causal to 0/1

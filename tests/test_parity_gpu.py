@@ -218,18 +218,19 @@ def test_wide_schedule_long_causal_rows_and_outliers(lib):
     assert torch.equal(out[:, :, 0].view(torch.int16), v[:, :, 0].view(torch.int16))
 
 
-# d = 64 shapes with N >= 2048 and fewer than 512 work-groups of 128 queries take
-# the key-split form of the 8-wave schedule: waves w and w+4 hold the same rows,
-# each over one half of the query tile's key tiles, merged at the end.  The
-# shapes give items with one tile (second half empty), odd counts (halves differ
-# by one) and even counts, ragged N and rows past N.
-SPLIT_SHAPES = [(1, 1, 2048), (1, 2, 2049), (2, 1, 2111), (1, 1, 3000)]
+# d = 64 shapes with N >= 2048 (causal: N >= 4096) and fewer than 512 work-groups
+# of 128 queries take the key-split form of the 8-wave schedule: waves w and w+4
+# hold the same rows, each over one half of the query tile's key tiles, merged at
+# the end.  The shapes give items with one tile (second half empty), odd counts
+# (halves differ by one) and even counts, ragged N and rows past N.
+SPLIT_SHAPES = {0: [(1, 1, 2048), (1, 2, 2049), (2, 1, 2111), (1, 1, 3000)],
+                1: [(1, 1, 4096), (1, 2, 4097), (2, 1, 4159), (1, 1, 4500)]}
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("causal", [0, 1])
 def test_key_split_schedule(lib, dtype, causal):
-    for B, H, N in SPLIT_SHAPES:
+    for B, H, N in SPLIT_SHAPES[causal]:
         assert lib.attn_fwd_schedule(B, H, N, 64, causal) == lib.ATTN_SCHEDULE_SPLIT
         print(f"\n[case] split B={B} H={H} N={N} {dtype} causal={causal}", flush=True)
         q, k, v = aw.make_inputs((B, H, N, 64), dtype, 9500 + N)
@@ -241,14 +242,31 @@ def test_key_split_schedule(lib, dtype, causal):
 
 def test_key_split_merge_with_outliers(lib):
     # the two halves reach very different row maxima: the merge rescales both
-    q, k, v = aw.make_inputs((2, 3, 2100, 64), "fp16", 9600, outlier_fraction=0.02, outlier_factor=30.0)
-    for causal in (0, 1):
-        assert lib.attn_fwd_schedule(2, 3, 2100, 64, causal) == lib.ATTN_SCHEDULE_SPLIT
+    for causal, N in ((0, 2100), (1, 4200)):
+        q, k, v = aw.make_inputs((2, 3, N, 64), "fp16", 9600, outlier_fraction=0.02, outlier_factor=30.0)
+        assert lib.attn_fwd_schedule(2, 3, N, 64, causal) == lib.ATTN_SCHEDULE_SPLIT
         for scale in (0.125, -0.2):
             out, lse = run_gpu(q, k, v, causal, scale)
-            rows = np.unique(np.concatenate([np.arange(200), np.random.default_rng(5).choice(2100, 300, replace=False), [2099]]))
+            rows = np.unique(np.concatenate([np.arange(200), np.random.default_rng(5).choice(N, 300, replace=False), [N - 1]]))
             assert_within_derived_bound(out, lse, q, k, v, causal, scale, rows=rows,
                                         label=f"split outliers causal={causal} scale={scale}")
+
+
+# Causal 4-wave grids whose single query tiles fit one round of two work-groups
+# per CU run them unpaired, longest first from both ends of one list: tile counts
+# that are odd or end inside a tile index's run of heads must still give every
+# tile to exactly one work-group (a missed tile leaves its rows unwritten).
+UNPAIRED_SHAPES = [(1, 3, 640, 64, "fp16"), (2, 5, 1100, 80, "bf16"), (1, 7, 1000, 128, "fp16"), (1, 1, 300, 64, "bf16")]
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype", UNPAIRED_SHAPES, ids=[f"{s[0]}x{s[1]}x{s[2]}x{s[3]}-{s[4]}" for s in UNPAIRED_SHAPES])
+def test_unpaired_causal_tiles(lib, B, H, N, d, dtype):
+    assert lib.attn_fwd_schedule(B, H, N, d, 1) == lib.ATTN_SCHEDULE_SMALL
+    print(f"\n[case] unpaired B={B} H={H} N={N} d={d} {dtype}", flush=True)
+    q, k, v = aw.make_inputs((B, H, N, d), dtype, 9800 + N + d)
+    out, lse = run_gpu(q, k, v, 1, 1.0 / math.sqrt(d))
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    assert_within_derived_bound(out, lse, q, k, v, 1, 1.0 / math.sqrt(d), label=f"unpaired B={B} H={H} N={N} d={d}")
 
 
 def test_small_schedule_d64(lib):
