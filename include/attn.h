@@ -129,9 +129,12 @@ int attn_fwd_window(const void* q, const void* k, const void* v, void* out, floa
  * (64 keys per key tile) that run in one short round, and every row of those
  * tiles is combined from its P partial results exactly as attn_lse_merge
  * (attn_bwd.h) documents: each partial is computed like attn_fwd over its key
- * range, its O rounded to `dtype`.  The result equals attn_fwd's up to that
- * extra rounding of the partial O (within a unit in the last place of `dtype`
- * of the exact row, typically).
+ * range, its O rounded to `dtype`.  Rows of the cut tiles therefore differ
+ * from attn_fwd's by that extra rounding of the partial O (the merge weights
+ * sum to 1, so at most one rounding of the row's weighted |V|).  The other
+ * rows run the 8-wave schedule: bitwise equal to attn_fwd where it uses that
+ * schedule too (attn_fwd_schedule returns ATTN_SCHEDULE_WIDE), else equal up
+ * to floating-point summation order.
  *
  *   workspace       : device pointer, 256-byte aligned, or NULL.  NULL, or a
  *                     shape that needs no split (attn_fwd_workspace_bytes returns
