@@ -277,6 +277,30 @@ def time_steps(call, steps: int, stream) -> dict:
     return {"ms_per_step": total_ms / steps, "per_launch": per_launch, "launch_ms": statistics.mean(per_launch)}
 
 
+COLD_L2_BYTES = 1 << 30   # written between cold-cache calls: past the 8 x 4 MB of L2 and the 256 MB Infinity Cache
+
+
+def time_steps_cold(call, steps: int, stream, scratch) -> dict:
+    """The K timed steps with cold caches: before each call the 1 GiB `scratch`
+    buffer is overwritten (outside the timed region), so the call finds its
+    inputs in HBM only.  Each call is timed between its own pair of events;
+    ms_per_step is their mean (the event records add a few microseconds, as in
+    time_steps' second loop)."""
+    import torch
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        scratch.fill_(i & 0xFF)
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    per_launch = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    mean = statistics.mean(per_launch)
+    return {"ms_per_step": mean, "per_launch": per_launch, "launch_ms": mean}
+
+
 def launch_stats(t: dict) -> dict:
     pl = sorted(t["per_launch"])
     return {"launch_ms_mean": round(t["launch_ms"], 5), "launch_ms_median": round(statistics.median(pl), 5),
@@ -654,6 +678,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--entry", choices=["auto", "attn_fwd"], default="auto",
                     help="forward entry point: auto uses attn_fwd_ws where it splits the last round")
+    ap.add_argument("--cold-l2", action="store_true",
+                    help="forward only: overwrite a 1 GiB buffer before each timed call (L2 and Infinity Cache "
+                         "cold), each call timed between its own events")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip the clock-under-load window (for profiler runs, which time every dispatch)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -731,7 +758,11 @@ def main():
             eta.attn_fwd(q, k, v, out, lse, causal, w.scale, stream=stream, window=args.window)
 
     warm = warm_up(call, args.warmup)
-    t = time_steps(call, args.steps, stream)
+    if args.cold_l2:
+        scratch = torch.empty(COLD_L2_BYTES, dtype=torch.uint8, device=dev)
+        t = time_steps_cold(call, args.steps, stream, scratch)
+    else:
+        t = time_steps(call, args.steps, stream)
     sclk = None if args.no_clock else ClockUnderLoad().measure(call)
     ms_per_step = t["ms_per_step"]
     flops = launch_flops(w, causal, args.window)
@@ -759,13 +790,19 @@ def main():
                    **launch_stats(t), "sclk": sclk,
                    "pct_of_peak_at_sclk": (round(100 * achieved / (MFMA_PEAK_TFLOPS * sclk["median_mhz"] / 2400.0), 2)
                                            if sclk and sclk.get("median_mhz") else None),
-                   "timing": "ms_per_step: one event pair around the K timed steps (also the roofline's launch "
-                             "duration); launch_ms_*: a second loop of K launches, each between its own events "
-                             "(those records add a few microseconds per launch)"},
+                   "l2": "cold" if args.cold_l2 else "warm",
+                   "timing": ("ms_per_step: the mean of the K calls, each between its own events after a 1 GiB "
+                              "buffer was overwritten (outside the events); launch_ms_*: the same calls")
+                             if args.cold_l2 else
+                             ("ms_per_step: one event pair around the K timed steps (also the roofline's launch "
+                              "duration); launch_ms_*: a second loop of K launches, each between its own events "
+                              "(those records add a few microseconds per launch)")},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(w.name, causal, args.window,
-                                                 key=(traffic_key(w.name, causal) + "-ws") if workspace is not None else None),
+                     # the committed counters were taken with warm caches
+                     "traffic": None if args.cold_l2 else measured_traffic(
+                         w.name, causal, args.window,
+                         key=(traffic_key(w.name, causal) + "-ws") if workspace is not None else None),
                      "kernel": f"attn_fwd_kernel<{w.d},{'bf16' if w.dtype == 'bf16' else 'f16'},{'causal' if causal else 'full'}>"
                                + (" with key-range parts, then lse_merge_kernel (achieved over both)" if workspace is not None else ""),
                      "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": w.algorithmic_bytes()},
