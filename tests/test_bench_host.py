@@ -57,3 +57,47 @@ def test_clock_reading_never_raises_without_a_gpu():
     assert "median_mhz" in r
     if r["median_mhz"] is None:
         assert r.get("error")
+
+
+def test_cold_cache_buffer_exceeds_the_caches():
+    """--cold-l2 overwrites more bytes than MI355X's caches hold between calls: eight
+    4 MB L2s and the 256 MB Infinity Cache."""
+    assert bench.COLD_L2_BYTES >= 2 * (8 * 4 * 2 ** 20 + 256 * 2 ** 20)
+
+
+def test_cold_cache_timing_flushes_outside_the_events():
+    """time_steps_cold overwrites the buffer before each call's start event, so the
+    flush is never inside a timed interval (checked on the order of the calls it
+    makes, with stand-ins for the stream events)."""
+    import sys
+    import types
+
+    log = []
+
+    class Event:
+        def __init__(self, enable_timing=False):
+            self.t = None
+
+        def record(self, stream=None):
+            log.append("record")
+            self.t = len(log)
+
+        def elapsed_time(self, other):
+            return float(other.t - self.t)
+
+    class Scratch:
+        def fill_(self, v):
+            log.append("flush")
+
+    fake = types.SimpleNamespace(cuda=types.SimpleNamespace(Event=Event, synchronize=lambda: None))
+    real = sys.modules.get("torch")
+    sys.modules["torch"] = fake
+    try:
+        t = bench.time_steps_cold(lambda: log.append("call"), 3, None, Scratch())
+    finally:
+        if real is not None:
+            sys.modules["torch"] = real
+        else:
+            del sys.modules["torch"]
+    assert log == ["flush", "record", "call", "record"] * 3
+    assert t["per_launch"] == [2.0, 2.0, 2.0] and t["ms_per_step"] == 2.0
