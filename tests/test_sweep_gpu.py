@@ -2,10 +2,12 @@
 one property at a time; these draw shape, head dim, type, mask, window, scale and
 outliers together from a fixed-seed generator, per schedule the library selects
 (4-wave, 4-wave unpaired causal, 8-wave, 8-wave key split, key-range parts
-through attn_fwd_ws), plus the backward.  Each case is checked against the
-float64 oracle with the derived bounds of the other tests (forward: per element
-and mean, lse; backward: the gradient bound), on every row or on a seeded
-sample of rows per head where a case has hundreds of heads.
+through attn_fwd_ws), plus the backward, the matrix product, the row softmax
+and the merge of key shards.  Each case is checked against the float64 oracle
+with the bars of the other tests (forward: the derived per-element and mean
+bounds, lse; backward: the gradient bound; the others: their own files' bars),
+on every row or on a seeded sample of rows per head where a case has hundreds
+of heads.
 
 The draw is fixed by SEED: a case's id names its shape and parameters, so a
 failure is reproduced by running that id alone."""
@@ -174,3 +176,110 @@ def test_backward_sweep(lib, c):
     q, k, v, do, out, lse = bwd_inputs(shape, c["dtype"], c["seed"], c["causal"], c["scale"])
     dq, dk, dv, _ = run_bwd(q, k, v, do, out, lse, c["causal"], c["scale"])
     check_bwd((dq, dk, dv), q, k, v, do, c["causal"], c["scale"], c["dtype"], str(c))
+
+
+# --- the later rows: matrix product, row softmax, merge of key shards ----------
+
+def _gemm_cases():
+    rng = np.random.default_rng(SEED + 2)
+    cases = []
+    for _ in range(16):
+        cases.append(dict(M=_length(rng, 1200), N=_length(rng, 1200), K=_length(rng, 600),
+                          b_layout=("kn", "nk")[int(rng.integers(2))],
+                          act=("none", "relu", "gelu_tanh")[int(rng.integers(3))],
+                          bias=bool(rng.random() < 0.75), dtype=("fp16", "bf16")[int(rng.integers(2))],
+                          seed=int(rng.integers(1 << 30))))
+    return cases
+
+
+GEMM = _gemm_cases()
+
+
+@pytest.mark.parametrize("c", GEMM, ids=[f"g{i:02d}-{c['M']}x{c['N']}x{c['K']}-{c['b_layout']}-{c['act']}"
+                                          f"{'-bias' if c['bias'] else ''}-{c['dtype']}" for i, c in enumerate(GEMM)])
+def test_gemm_sweep(lib, c):
+    """M, N, K drawn around and between the 256-row tiles, the 64-wide k steps and the
+    8-element chunks (K not a multiple of 8 goes through the binding's zero padding)."""
+    from test_gemm_gpu import check as check_gemm
+    print(f"\n[case] {c}", flush=True)
+    a, b, bias = aw.make_gemm(c["M"], c["N"], c["K"], c["dtype"], c["b_layout"], c["seed"])
+    bias = bias if c["bias"] else None
+    out = eta.gemm_bias_act(a.cuda(), b.cuda(), None if bias is None else bias.cuda(), c["act"], c["b_layout"])
+    torch.cuda.synchronize()
+    check_gemm(out.cpu(), a, b, bias, c["act"], c["b_layout"], c["dtype"], str(c))
+
+
+def _softmax_cases():
+    rng = np.random.default_rng(SEED + 3)
+    cases = []
+    for _ in range(12):
+        if rng.random() < 0.5:
+            cols = int(round(math.exp(rng.uniform(0.0, math.log(200000)))))
+        else:
+            cols = int(rng.integers(30000, 200001))
+        rows = int(rng.integers(1, max(2, min(300, 4_000_000 // cols)) + 1))
+        cases.append(dict(rows=rows, cols=cols, dtype=("f32", "bf16", "fp16")[int(rng.integers(3))],
+                          sigma=float(rng.choice((0.5, 1.0, 4.0, 20.0))), masked=float(rng.choice((0.0, 0.0, 0.3))),
+                          seed=int(rng.integers(1 << 30))))
+    return cases
+
+
+SOFTMAX = _softmax_cases()
+
+
+@pytest.mark.parametrize("c", SOFTMAX, ids=[f"s{i:02d}-{c['rows']}x{c['cols']}-{c['dtype']}-sigma{c['sigma']:g}"
+                                             f"{'-masked' if c['masked'] else ''}" for i, c in enumerate(SOFTMAX)])
+def test_softmax_sweep(lib, c):
+    """Row lengths from 1 to 2e5 (in registers up to 65536, tiled beyond), score
+    spreads up to sigma = 20, and rows with a share of -inf (masked) entries."""
+    from test_softmax_gpu import check as check_softmax
+    print(f"\n[case] {c}", flush=True)
+    x = aw.make_rows(c["rows"], c["cols"], c["dtype"], c["seed"], c["sigma"])
+    if c["masked"]:
+        keep = np.random.default_rng(c["seed"] + 1).random((c["rows"], c["cols"])) >= c["masked"]
+        keep[:, 0] = True                                   # every row keeps one entry
+        x = x.masked_fill(torch.from_numpy(~keep), -float("inf"))
+    y = eta.softmax_rows(x.cuda())
+    torch.cuda.synchronize()
+    check_softmax(y, x, c["dtype"], str(c))
+
+
+def _merge_cases():
+    rng = np.random.default_rng(SEED + 4)
+    cases = []
+    for _ in range(10):
+        cases.append(dict(G=int(rng.integers(1, 11)), R=_length(rng, 40000), d=int(rng.choice(D_CHOICES)),
+                          dtype=("fp16", "bf16")[int(rng.integers(2))], empty=float(rng.choice((0.0, 0.2, 0.6))),
+                          seed=int(rng.integers(1 << 30))))
+    return cases
+
+
+MERGE = _merge_cases()
+
+
+@pytest.mark.parametrize("c", MERGE, ids=[f"m{i:02d}-G{c['G']}-R{c['R']}-d{c['d']}-{c['dtype']}-empty{c['empty']:g}"
+                                          for i, c in enumerate(MERGE)])
+def test_merge_sweep(lib, c):
+    """G from 1 to 10 shards (past the eight read per round), lse spread over
+    about 20 nats, and a share of -inf entries (shards with no key for a row),
+    which leaves some rows with every shard empty."""
+    from oracle import backward as ob
+    from test_bwd_gpu import U_OUT
+    print(f"\n[case] {c}", flush=True)
+    G, R, d = c["G"], c["R"], c["d"]
+    g = np.random.default_rng(c["seed"])
+    o_parts = torch.from_numpy(g.standard_normal((G, R, d)).astype(np.float32)).to(aw.DTYPES[c["dtype"]])
+    l_np = (g.standard_normal((G, R)) * 5.0 + 3.0).astype(np.float32)
+    l_np[g.random((G, R)) < c["empty"]] = -np.inf
+    l_parts = torch.from_numpy(l_np)
+    o, lse = eta.attn_lse_merge(o_parts.cuda(), l_parts.cuda())
+    torch.cuda.synchronize()
+    ro, rl = ob.lse_merge(o_parts.double().numpy(), l_parts.double().numpy())
+    got_o, got_l = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    empty = ~np.isfinite(rl)
+    assert (np.isneginf(got_l) == empty).all()
+    assert (got_o[empty] == 0).all()
+    ok = ~empty
+    big = np.abs(o_parts.double().numpy()).max(axis=0)
+    assert (np.abs(got_o - ro)[ok] <= (U_OUT[c["dtype"]] * np.abs(ro) + 1e-5 * (1 + big))[ok]).all()
+    assert (np.abs(got_l[ok] - rl[ok]) <= 1e-5 * (1 + np.abs(rl[ok]))).all()
