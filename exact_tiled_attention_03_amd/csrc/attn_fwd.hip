@@ -117,7 +117,7 @@ struct FwdArgs {
     int N;
     int BH;
     int nqt;           // query tiles per head
-    int ngroups;       // work-groups per head: causal pairs tiles (i, nqt-1-i), else nqt
+    int ngroups;       // work-groups per head: causal without a window pairs tiles (i, nqt-1-i), else nqt
     float c;           // |scale| * log2(e), > 0
     unsigned qsign;    // 0x80008000 when scale < 0 (Q negated exactly), else 0
     int window;        // 0: none; W in [1, N): key j kept for query i only if i - W < j (and j < i + W if not causal)
@@ -635,7 +635,10 @@ void attn_fwd_kernel(FwdArgs a) {
         bh = g / a.ngroups;
         grp = g - bh * a.ngroups;
     }
-    int nitems = CAUSAL && grp != a.nqt - 1 - grp ? 2 : 1;
+    // a causal tile's keys grow with its index, so tiles i and nqt-1-i share a
+    // unit; with a window every tile has about W keys and runs alone (a pair
+    // would only put two tiles in sequence on one work-group)
+    int nitems = CAUSAL && !WIN && grp != a.nqt - 1 - grp ? 2 : 1;
     int qt_one = -1;
     if (CAUSAL && WAVES == 4 && !WIN && a.unpaired) {
         // All U tiles in one round of two work-groups per CU.  With the tiles listed
@@ -651,7 +654,7 @@ void attn_fwd_kernel(FwdArgs a) {
         nitems = 1;
     }
     for (int item = 0; item < nitems; ++item, first = false) {
-        const int qt = qt_one >= 0 ? qt_one : (CAUSAL ? (item == 0 ? a.nqt - 1 - grp : grp) : grp);
+        const int qt = qt_one >= 0 ? qt_one : (CAUSAL && !WIN ? (item == 0 ? a.nqt - 1 - grp : grp) : grp);
         const int q0 = qt * BMQ;
         // Q rows come through LDS (q_issue / q_read) in every schedule
         w.begin(a, bh, q0 + 32 * (SPLIT ? wave & 3 : wave));
@@ -932,7 +935,7 @@ hipError_t launch_waves(FwdArgs a, hipStream_t stream, int cus) {
     const long long nqt = ((long long)a.N + BM - 1) / BM;
     a.nqt = (int)nqt;
     a.unpaired = WAVES == 4 && !WIN && use_unpaired(a.BH, a.N, CAUSAL, a.window, cus) ? 1 : 0;
-    a.ngroups = CAUSAL && !a.unpaired ? (int)((nqt + 1) / 2) : (int)nqt;
+    a.ngroups = CAUSAL && !WIN && !a.unpaired ? (int)((nqt + 1) / 2) : (int)nqt;
     const unsigned units = (unsigned)a.ngroups * (unsigned)a.BH;
     a.nwhole = (int)units;
     unsigned grid = units;

@@ -171,7 +171,7 @@ long long attn_fwd_workspace_bytes(int B, int H, int N, int d, int causal);
  * Returns ATTN_SCHEDULE_SMALL (4 waves, 128 queries per work-group, two
  * work-groups per CU; causal query tiles in pairs (i, T-1-i) per work-group,
  * or one per work-group, longest first, when all of them fit one round of two
- * per CU), ATTN_SCHEDULE_WIDE (8 waves, 256 queries per work-group, one per
+ * per CU; with a window one tile per work-group), ATTN_SCHEDULE_WIDE (8 waves, 256 queries per work-group, one per
  * CU), ATTN_SCHEDULE_SPLIT (d = 64 and N >= 2048 where the small schedule
  * would give fewer than 512 work-groups, except causal problems below 4096
  * keys whose tiles fit the unpaired round: 8 waves, 128 queries per
