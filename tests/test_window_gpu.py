@@ -108,3 +108,21 @@ def test_window_negative_rejected(lib):
     assert ei.value.status == 11
     torch.cuda.synchronize()
     assert (out == 7.0).all()
+
+
+# Causal windowed problems give every query tile its own work unit (no causal
+# pairs): odd tile counts, for both launch shapes, every row of the checked heads.
+@pytest.mark.parametrize("B,H,N,d,w", [(8, 64, 5 * 256 - 3, 64, 300), (1, 3, 7 * 128 - 5, 80, 200)],
+                         ids=["wide-5-tiles", "small-7-tiles"])
+def test_window_causal_every_tile_of_odd_counts(lib, B, H, N, d, w):
+    want = eta.ATTN_SCHEDULE_WIDE if B * H >= 512 else eta.ATTN_SCHEDULE_SMALL
+    assert eta.attn_fwd_schedule(B, H, N, d, 1) == want
+    print(f"\n[case] window causal B={B} H={H} N={N} d={d} W={w}", flush=True)
+    q, k, v = aw.make_inputs((B, H, N, d), "fp16", 9700 + N)
+    out, lse = run_gpu(q, k, v, 1, 1 / math.sqrt(d), window=w)
+    heads = [(0, 0), (B - 1, H - 1), (B // 2, H // 2)]
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        assert_within_derived_bound(out[sl], lse[sl], q[sl], k[sl], v[sl], 1, 1 / math.sqrt(d), window=w,
+                                    label=f"head ({b},{h}) N={N} W={w}")
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
