@@ -449,14 +449,15 @@ struct Wave {
     // P.V MFMAs sum the rounded ones instead)
     __device__ __forceinline__ void probs(const f32x16_t (&s)[SB], u32x4_t (&pf)[KK]) {
         const float nm = m > kNegInf ? -m : 0.f;
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
+        float part[4];
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             float p[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kk >> 1][8 * (kk & 1) + i], c, nm));
-                if constexpr (!ONES) part[i & 3] += p[i];
+                // the chains start at their first probability (p >= 0, so 0 + p = p exactly)
+                if constexpr (!ONES) part[i & 3] = kk == 0 && i < 4 ? p[i] : part[i & 3] + p[i];
             }
             pf[kk] = u32x4_t{E::pack2(p[0], p[1]), E::pack2(p[2], p[3]), E::pack2(p[4], p[5]), E::pack2(p[6], p[7])};
         }
