@@ -69,14 +69,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def source_hash(path: str = KERNEL_SOURCE) -> str:
-    """Hash of a kernel source's code: comments and whitespace are dropped, so that
-    editing a comment does not invalidate counters taken on the same code."""
+    """Hash of a kernel source's code and of the flags it alone is compiled with:
+    comments and whitespace are dropped, so that editing a comment does not
+    invalidate counters taken on the same code."""
     import re
+    from exact_tiled_attention_03_amd.build import source_flags
     with open(path) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
-    text = " ".join(text.split())
+    text = " ".join(text.split() + list(source_flags(path)))
     return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 

@@ -61,6 +61,9 @@ typedef enum {
  *
  *   q, k, v : device pointers, contiguous row-major [B, H, N, d] of `dtype`
  *             (element (b,h,i,c) at offset ((b*H + h)*N + i)*d + c).  Read only.
+ *             Elements are finite numbers; a row whose scores meet a NaN or an
+ *             infinite element gets unspecified out and lse values (the kernels
+ *             assume no NaN arises when they form the running row max).
  *   out     : device pointer, contiguous [B, H, N, d] of `dtype`.  Every element
  *             is written: out[b,h,i,:] = sum_j softmax_j(scale * q_i . k_j) v_j,
  *             rounded to nearest even from an fp32 accumulator.
